@@ -1,0 +1,309 @@
+"""Pins of the oracle's low-precision AdamW step (MS-AMP O2 and O3 layouts).
+
+Sources: MS-AMP "Optimization Level" page (section O2: first moment in FP8,
+second moment in FP16; section O3: FP16 master weight + FP8 regular weight;
+the optimization-level table) and the MS-AMP README (Usage: the recognized
+optimizers are torch.optim.Adam / AdamW; the O2 memory claim).
+
+What pins the step, other than the oracle itself:
+  * exact-rational evaluation of every binary32 operation of the step
+    (tests/exact_fp.py) with brute-force FP8/FP16 encoders, bit for bit, on
+    hand-sized examples and on random tiny tensors;
+  * hand-computed bit patterns of the worked examples (one element, and three
+    elements over two steps), written below as literals;
+  * the binary32-storage special case against torch.optim.AdamW;
+  * the quantized trajectory staying within FP8/FP16 storage error of the
+    binary32 trajectory;
+  * the 62.5% optimizer-state saving of O2 (FP32+FP32 -> FP8+FP16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.exact_fp import F, brute_encode_f16, brute_encode_fp8, f16_value, fp8_value, float_to_bits
+
+HP = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+
+
+# ---------------------------------------------------------------------------
+# Exact-rational reference of one step (same readings, different arithmetic)
+# ---------------------------------------------------------------------------
+
+def exact_constants(step, lr, betas, eps, weight_decay):
+    b1, b2 = betas
+    bc1 = 1.0 - b1 ** step
+    bc2 = 1.0 - b2 ** step
+    vals = [b1, 1.0 - b1, b2, 1.0 - b2, eps, lr / bc1, 1.0 / bc2 ** 0.5, 1.0 - lr * weight_decay]
+    return [F.of(v) for v in vals]
+
+
+def exact_scale(amax: F, fmax: float) -> F:
+    a = amax.q
+    if a <= 0:
+        return F.of(1.0)
+    s = F.of(fmax) / amax
+    if (s.b & 0x7F800000) == 0x7F800000 or s.q <= 0:
+        return F.of(1.0)
+    return s
+
+
+def exact_step(state, g32, gfmt, step, hp=HP, level="O2"):
+    """One step on python lists of bit patterns. state: dict with w (fp16
+    bits), v (fp16 bits), m (E4M3 codes), m_si (F), and for O3 w8, w8_meta."""
+    B1, OB1, B2, OB2, EPS, SS, IBS, DEC = exact_constants(step, **hp)
+    fmax_g = O.fp8_max(gfmt)
+    # gradient quantization
+    amax_g = max(float_to_bits(float(x)) & 0x7FFFFFFF for x in g32) if len(g32) else 0
+    s_g = exact_scale(F(amax_g), fmax_g)
+    si_g = F.of(1.0) / s_g
+    qg = []
+    for x in g32:
+        xs = F.of(float(x)) * s_g
+        qg.append(brute_encode_fp8(xs.q, gfmt, bool(xs.b >> 31)))
+    # pass 1
+    gs, m1s = [], []
+    for i in range(len(g32)):
+        g = fp8_value(qg[i], gfmt) * si_g
+        m0 = fp8_value(state["m"][i], 0) * state["m_si"]
+        m1 = F.fma(B1, m0, OB1 * g)
+        gs.append(g)
+        m1s.append(m1)
+    amax_m = F(max((m.b & 0x7FFFFFFF) for m in m1s) if m1s else 0)
+    s_m = exact_scale(amax_m, 448.0)
+    si_m = F.of(1.0) / s_m
+    # pass 2
+    for i in range(len(g32)):
+        g, m1 = gs[i], m1s[i]
+        v1 = F.fma(B2, f16_value(state["v"][i]), OB2 * (g * g))
+        den = F.fma(v1.sqrt(), IBS, EPS)
+        w1 = F.fma(-SS, m1 / den, f16_value(state["w"][i]) * DEC)
+        state["v"][i] = brute_encode_f16(v1.q, bool(v1.b >> 31))
+        state["w"][i] = brute_encode_f16(w1.q, bool(w1.b >> 31))
+        ms = m1 * s_m
+        state["m"][i] = brute_encode_fp8(ms.q, 0, bool(ms.b >> 31))
+    state["m_meta"] = (amax_m.b, s_m.b, si_m.b)
+    state["m_si"] = si_m
+    if level == "O3":
+        amax_w = F(max((f16_value(h).b & 0x7FFFFFFF) for h in state["w"]) if state["w"] else 0)
+        s_w = exact_scale(amax_w, 448.0)
+        codes = []
+        for h in state["w"]:
+            xs = f16_value(h) * s_w
+            codes.append(brute_encode_fp8(xs.q, 0, bool(xs.b >> 31)))
+        state["w8"] = codes
+        state["w8_meta"] = (amax_w.b, s_w.b, (F.of(1.0) / s_w).b)
+    return qg, (amax_g, s_g.b, si_g.b)
+
+
+def new_exact_state(w_bits):
+    n = len(w_bits)
+    return {"w": [int(x) for x in w_bits], "v": [0] * n, "m": [0] * n, "m_si": F.of(1.0)}
+
+
+def u32(a):
+    return [int(x) for x in np.asarray(a, np.float32).view(np.uint32)[:3]]
+
+
+def run_both(w_bits, grads, gfmt, level, hp=HP):
+    """Run the oracle and the exact reference side by side; assert bitwise
+    agreement after every step. Returns the oracle state."""
+    ost = O.TensorState(np.array(w_bits, np.uint16), level)
+    est = new_exact_state(w_bits)
+    for t, g in enumerate(grads, start=1):
+        g = np.asarray(g, np.float32)
+        (qg, gmeta), = O.step_list([ost], [g], gfmt, t, **hp)
+        eqg, egmeta = exact_step(est, g, gfmt, t, hp, level)
+        assert list(qg) == eqg, ("grad codes", t)
+        assert u32(gmeta) == list(egmeta), ("grad meta", t)
+        assert list(ost.m) == est["m"], ("m codes", t)
+        assert u32(ost.m_meta) == list(est["m_meta"]), ("m meta", t)
+        assert list(ost.v) == est["v"], ("v", t)
+        assert list(ost.w) == est["w"], ("w", t)
+        if level == "O3":
+            assert list(ost.w8) == est["w8"], ("w8", t)
+            assert u32(ost.w8_meta) == list(est["w8_meta"]), ("w8 meta", t)
+    return ost
+
+
+# ---------------------------------------------------------------------------
+# Hand-computed worked examples
+# ---------------------------------------------------------------------------
+
+def test_constants_hand_computed():
+    k1 = O.adamw_constants(1, **HP).view(np.uint32)
+    k2 = O.adamw_constants(2, **HP).view(np.uint32)
+    # B1 OB1 B2 OB2 EPS SS IBS DEC
+    assert [hex(x) for x in k1] == ["0x3f666666", "0x3dcccccd", "0x3f7fbe77", "0x3a83126f",
+                                    "0x322bcc77", "0x3c23d70a", "0x41fcfb72", "0x3f7fff58"]
+    assert hex(k2[5]) == "0x3bac7692" and hex(k2[6]) == "0x41b2ee20"
+    assert [e.b for e in exact_constants(1, **HP)] == [int(x) for x in k1]
+
+
+@pytest.mark.parametrize("gfmt", [O.E4M3, O.E5M2])
+def test_worked_example_one_element(gfmt):
+    """w = fp16(0.02), g = 1e-3, t = 1 (O2, then the O3 weight copy)."""
+    w = O.f16_encode(np.array([0.02], np.float32))
+    assert int(w[0]) == 0x251F
+    st = run_both([0x251F], [[1e-3]], gfmt, "O3")
+    # hand-computed: gradient scale, new moment and its scale, outputs
+    assert int(st.w[0]) == 0x24DD  # 0.0189972
+    assert int(st.v[0]) == 0x0000  # (1-b2)*g^2 = 1e-9 underflows binary16
+    assert int(st.m[0]) == 0x7E
+    assert u32(st.m_meta) == [0x38D1B718, 0x4A88B800, 0x346FACAD]
+    assert int(st.w8[0]) == 0x7E
+    assert u32(st.w8_meta) == [0x3C9BA000, 0x46B83CDD, 0x3831DB6E]
+    qg, gmeta = O.quantize_fp8(np.array([1e-3], np.float32), gfmt)
+    if gfmt == O.E4M3:
+        assert u32(gmeta) == [0x3A83126F, 0x48DABFFF, 0x3615CBED] and qg[0] == 0x7E
+    else:
+        assert u32(gmeta) == [0x3A83126F, 0x4C5ABFFF, 0x3295CBED] and qg[0] == 0x7B
+
+
+def test_worked_example_three_elements_two_steps():
+    st = run_both([0x3800, 0xA51F, 0x0000], [[0.5, 1e-3, 0.0], [-0.25, 2e-3, 0.0]], O.E4M3, "O3")
+    # after step 2 (hand-computed)
+    assert [int(x) for x in st.w] == [0x37FB, 0xA5A8, 0x0000]
+    assert [int(x) for x in st.v] == [0x0D1E, 0x0000, 0x0000]
+    assert [int(x) for x in st.m] == [0x7E, 0x4D, 0x00]
+    assert u32(st.m_meta)[1:] == [0x46AF0000, 0x383B3EE7]
+    assert [int(x) for x in st.w8] == [0x7E, 0xDA, 0x00]
+    assert u32(st.w8_meta)[1:] == [0x44608C58, 0x3A91EDB7]
+
+
+def test_worked_example_step1_three_elements():
+    st = run_both([0x3800, 0xA51F, 0x0000], [[0.5, 1e-3, 0.0]], O.E4M3, "O3")
+    assert [int(x) for x in st.w] == [0x37FC, 0xA561, 0x0000]
+    assert [int(x) for x in st.v] == [0x0C19, 0x0000, 0x0000]
+    assert [int(x) for x in st.m] == [0x7E, 0x36, 0x00]
+    assert u32(st.m_meta)[1:] == [0x460C0000, 0x38EA0EA1]
+    assert [int(x) for x in st.w8] == [0x7E, 0xD9, 0x00]
+
+
+def test_worked_example_zero_gradient():
+    """All-zero gradient: scale 1, m = 0, den = eps, and the decay of w is
+    below half a binary16 ulp, so w is unchanged."""
+    w = [0x251F, 0xBC00]
+    st = run_both(w, [[0.0, 0.0]], O.E4M3, "O2")
+    assert [int(x) for x in st.w] == w
+    assert list(st.v) == [0, 0] and list(st.m) == [0, 0]
+    assert list(st.m_meta[:3]) == [0.0, 1.0, 1.0]
+
+
+@pytest.mark.parametrize("level", ["O2", "O3"])
+@pytest.mark.parametrize("gfmt", [O.E4M3, O.E5M2])
+def test_random_tiny_tensors_match_exact_arithmetic(level, gfmt):
+    rng = np.random.default_rng(17 + gfmt + (level == "O3") * 2)
+    n = 6
+    w = O.f16_encode((rng.standard_normal(n) * 0.5).astype(np.float32))
+    hp = dict(lr=3e-2, betas=(0.8, 0.95), eps=1e-6, weight_decay=0.1)
+    grads = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 1, n)).astype(np.float32) for _ in range(3)]
+    grads[1][2] = 0.0
+    run_both(list(w), grads, gfmt, level, hp)
+
+
+# ---------------------------------------------------------------------------
+# Special case: binary32 storage is PyTorch's AdamW
+# ---------------------------------------------------------------------------
+
+def test_fp32_storage_matches_torch_adamw():
+    rng = np.random.default_rng(0)
+    n = 4096
+    lr, betas, eps, wd = 2e-2, (0.8, 0.95), 1e-6, 0.1
+    w0 = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.AdamW([p], lr=lr, betas=betas, eps=eps, weight_decay=wd, foreach=False)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w = w0.copy()
+    mag = np.zeros(n)  # running |g| average: the scale of the rounding in m
+    for t in range(1, 11):
+        # magnitudes from 1e-9 to 1: eps matters for the small ones
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-9, 0, n)).astype(np.float32)
+        mag = betas[0] * mag + (1 - betas[0]) * np.abs(g)
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        O.adamw_f32_tensor(g, m, v, w, t, lr=lr, betas=betas, eps=eps, weight_decay=wd)
+        st = opt.state[p]
+        # The rounding order differs (lerp, two-step addcmul, division by
+        # sqrt(bc2)), which leaves a few ulps per step. m can cancel, so its
+        # bound is relative to the running |g| average; v has no cancellation.
+        assert (np.abs(m - st["exp_avg"].numpy()) <= 1e-5 * mag).all()
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-5, atol=1e-30)
+        # weights that cross zero carry the rounding of lr-sized updates:
+        # absolute tolerance one millionth of lr
+        np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-5, atol=1e-6 * lr)
+
+
+def test_quantized_trajectory_tracks_fp32_trajectory():
+    """O2 storage error only: after 10 steps w stays within the accumulated
+    FP8-m / FP16 rounding of the binary32 AdamW trajectory."""
+    rng = np.random.default_rng(2)
+    n = 20000
+    lr = 1e-3
+    w16 = O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32))
+    st = O.TensorState(w16, "O2")
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w = O.f16_decode(w16)
+    for t in range(1, 11):
+        g = rng.standard_normal(n).astype(np.float32)  # large enough that v never underflows
+        O.step_list([st], [g], O.E4M3, t, **HP)
+        O.adamw_f32_tensor(g, m, v, w, t, **HP)
+    diff = np.abs(O.f16_decode(st.w).astype(np.float64) - w)
+    # per step at most ~1/16 of an lr-sized update from m and the FP8 grad,
+    # plus half a binary16 ulp of w (< 2^-17 near 0.06)
+    assert diff.max() < 10 * (lr * 0.35 + 2.0 ** -17)
+    assert np.median(diff) < 10 * lr * 0.05
+    # m decodes close to the binary32 moment: the E4M3 rounding of m and g
+    # (up to 2^-4 relative each step) accumulates over the steps, decaying by
+    # b1, so the error stays a small fraction of the moment's range
+    md = O.fp8_decode(st.m, O.E4M3) * st.m_meta[2]
+    err = np.abs(md - m)
+    assert err.max() <= 0.25 * np.abs(m).max()
+    assert np.median(err / np.maximum(np.abs(m), 1e-3)) < 2.0 ** -4
+
+
+def test_v_underflow_at_small_gradient_scale_is_reproduced():
+    """(1-b2)*g^2 falls below half the smallest binary16 subnormal for
+    |g| < ~5.5e-3, so the stored second moment is +0 at gradient scale 1e-3,
+    and a binary16 subnormal at scale 1e-2. The step still uses the binary32
+    v1 in the denominator of the same step."""
+    rng = np.random.default_rng(4)
+    n = 100_000
+    for sigma, zero_frac_lo, zero_frac_hi in ((1e-3, 0.999, 1.0), (1e-2, 0.0, 0.7)):
+        st = O.TensorState(O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32)), "O2")
+        g = (rng.standard_normal(n) * sigma).astype(np.float32)
+        O.step_list([st], [g], O.E4M3, 1, **HP)
+        zero = (st.v == 0).mean()
+        assert zero_frac_lo <= zero <= zero_frac_hi, (sigma, zero)
+        if sigma == 1e-2:
+            nz = st.v[st.v != 0]
+            assert (nz < 0x0400).mean() > 0.9  # mostly subnormal
+
+
+@pytest.mark.parametrize("level", ["O2", "O3"])
+def test_step_invariants(level):
+    rng = np.random.default_rng(8)
+    n = 12345
+    st = O.TensorState(O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32)), level)
+    for t in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        O.step_list([st], [g], O.E4M3, t, **HP)
+        assert (st.m & 0x7F).max() == 0x7E  # the new moment fills the E4M3 range
+        assert (st.m & 0x7F).max() != 0x7F  # never NaN
+        if level == "O3":
+            assert (st.w8 & 0x7F).max() == 0x7E
+            amax_w = np.abs(O.f16_decode(st.w)).max()
+            assert st.w8_meta[0] == amax_w
+            assert st.w8_meta[1] == O.scale(amax_w, 448.0)
+
+
+def test_optimizer_state_saving_is_62_5_percent():
+    """FP32+FP32 (8 B/param) -> FP8 first moment + FP16 second moment
+    (3 B/param) saves 5/8 of optimizer-state memory."""
+    st = O.TensorState(np.zeros(1000, np.uint16), "O2")
+    state_bytes = st.m.itemsize + st.v.itemsize
+    assert state_bytes == O.STATE_BYTES_FP8_FP16 == 3
+    saving = 1 - state_bytes / O.STATE_BYTES_FP32_FP32
+    assert saving == 0.625
