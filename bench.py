@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 AdamW hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+per-tensor amax of the binary32 gradients, their saturating FP8 quantize,
+then the low-precision AdamW step (O2: two passes + meta finalize; O3: three
+passes + finalize), all through the C ABI of libmsamp.so. Inputs (weights,
+states and two sets of binary32 gradients, alternated between steps) are
+resident in HBM before the timed region starts.
+
+Default workload: the Llama-2-7B parameter list (291 tensors, 6,738,415,616
+parameters) in the O2 layout with E4M3 gradients.
+
+Prints one JSON line: params updated per second over the whole path
+(`value`), the achieved algorithmic HBM bandwidth, the roofline entry of the
+dominant kernel (measured with HIP events on the launch stream during the
+timed region) and the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+# algorithmic bytes per parameter
+GRAD_AMAX_BYTES = 4          # read f32
+GRAD_QUANTIZE_BYTES = 4 + 1  # read f32, write FP8
+PASS1_BYTES = 1 + 1          # read grad FP8, exp_avg FP8
+PASS2_BYTES = 6 + 5          # read g, m, v, w; write m, v, w
+PASS3_BYTES = 2 + 1          # read master FP16, write FP8 copy
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_adamw_optimizer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama2_7b",
+                   help="llama2_7b (default), llama2_13b, gpt2_small, single_1m, stress")
+    p.add_argument("--shard", type=int, default=1,
+                   help="keep 1/N of every tensor (one data-parallel rank's share)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--no-profile", action="store_true",
+                   help="do not bracket kernels with HIP events")
+    p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                   help="only run a device-to-device copy of this many GiB (counter calibration)")
+    return p.parse_args()
+
+
+def calibrate_copy(gib: float) -> None:
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
+
+
+class State:
+    """Device state of a workload plus two resident binary32 gradient sets."""
+
+    def __init__(self, w, device):
+        import torch
+
+        import bit_adamw_optimizer_amd as M
+        from bit_adamw_optimizer_amd import workloads as W
+
+        self.w = w
+        self.weights = W.init_weights(w, device)
+        st = M.allocate_state(self.weights, w.level)
+        self.exp_avg_meta = st["exp_avg_meta"]
+        self.weight_fp8_meta = st.get("weight_fp8_meta")
+        self.tl_m = M.TensorList(st["exp_avg"], "u8", "exp_avg")
+        self.tl_v = M.TensorList(st["exp_avg_sq"], "f16", "exp_avg_sq")
+        self.tl_w = M.TensorList(self.weights, "f16", "weight")
+        self.tl_w8 = M.TensorList(st["weight_fp8"], "u8", "weight_fp8") if w.level == "O3" else None
+        self.grad_q = M.TensorList([torch.empty(k, dtype=torch.uint8, device=device) for k in w.numel],
+                                   "u8", "grad_q")
+        self.grad_meta = M.new_meta(w.n, device)
+        self.grad_sets = []
+        for s in (1, 2):
+            g = [W.grad_tensor(w, t, s, device) for t in range(w.n)]
+            self.grad_sets.append(M.TensorList(g, "f32", "grad_f32"))
+        torch.cuda.synchronize()
+
+    def step(self, step: int) -> None:
+        import bit_adamw_optimizer_amd as M
+
+        w = self.w
+        g32 = self.grad_sets[(step - 1) % 2]
+        M.amax(g32, self.grad_meta)
+        M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
+        if w.level == "O2":
+            M.adamw_o2_step(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+                            self.tl_v, self.tl_w, step=step, **w.hparams())
+        else:
+            M.adamw_o3_step(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+                            self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step,
+                            **w.hparams())
+
+
+def cpu_baseline(w, device, threads: int) -> dict:
+    """The oracle on a bounded sample of the workload: the tensors of the
+    first layer (one full step each: gradient amax + quantize + the O2/O3
+    step), one thread per tensor."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from bit_adamw_optimizer_amd import workloads as W
+
+    idx = [t for t, nm in enumerate(w.names) if nm.startswith("layers.0.")]
+    if not idx:
+        idx = sorted(range(w.n), key=lambda t: -w.numel[t])[:8]
+    sub = w.subset(idx)
+    weights = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in W.init_weights(sub, device)]
+    grads = [W.grad_tensor(sub, t, 1, device).cpu().numpy() for t in range(sub.n)]
+    states = [O.TensorState(x, w.level) for x in weights]
+    nthreads = max(1, min(threads, len(idx)))
+    t0 = time.perf_counter()
+    O.step_list(states, grads, w.grad_fmt, 1, threads=nthreads, **w.hparams())
+    dt = time.perf_counter() - t0
+    return {"value": sub.params / dt, "unit": "params/s", "cores": nthreads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "%d tensors (%s), %d params, one step (grad amax + quantize + %s step), "
+                      "one oracle thread per tensor" % (sub.n, ", ".join(sub.names[:3]) + ", ...",
+                                                         sub.params, w.level)}
+
+
+def traffic_from_profiles(kernel: str, workload: str, params: int):
+    """HBM bytes per launch from committed counter runs, when they were taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return 0
+
+    import bit_adamw_optimizer_amd as M
+    from bit_adamw_optimizer_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    M.lib()
+    w = W.make(args.workload, shard=args.shard)
+    print("bench: %s, %s, %d tensors, %d params; setting up" % (w.name, w.level, w.n, w.params),
+          file=sys.stderr, flush=True)
+    st = State(w, device)
+
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        st.step(step)
+    torch.cuda.synchronize()
+
+    if not args.no_profile:
+        M.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step += 1
+        st.step(step)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = {}
+    if not args.no_profile:
+        M.profile_enable(False)
+        for k in M.KERNELS:
+            n, ms = M.profile_read(k)
+            if n:
+                kernels[k] = {"launches": n, "avg_ms": ms / n}
+
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    P = w.params
+    step_bytes = PASS1_BYTES + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+    path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
+    gbps = path_bytes * P / (ms_per_step * 1e-3) / 1e9
+
+    per_kernel_bytes = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES,
+                        "step_pass1": PASS1_BYTES, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
+                        "o3_pass3": PASS3_BYTES}
+    breakdown = {}
+    for k, d in kernels.items():
+        e = {"avg_ms": round(d["avg_ms"], 4), "launches": d["launches"]}
+        if k in per_kernel_bytes:
+            e["GB/s"] = round(per_kernel_bytes[k] * P / (d["avg_ms"] * 1e-3) / 1e9, 1)
+        breakdown[k] = e
+    dom = "o2_pass2" if w.level == "O2" else "o3_pass2"
+    roofline = None
+    if dom in kernels:
+        achieved = per_kernel_bytes[dom] * P / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic_from_profiles(dom, w.name, P),
+                    "algorithmic_bytes_per_launch": per_kernel_bytes[dom] * P}
+    opt_ms = sum(kernels[k]["avg_ms"] for k in ("step_pass1", dom, "o3_pass3", "finalize")
+                 if k in kernels)
+    result = {
+        "metric": "params updated/sec and achieved HBM GB/s (% of peak) for O2/O3 FP8 AdamW step",
+        "value": P / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: %s FP8 AdamW step, %d tensors, %d params, %s grads "
+                               "(amax + quantize + step per iteration)"
+                               % (w.name, w.level, w.n, P, "E4M3" if w.grad_fmt == 0 else "E5M2"),
+                   "level": w.level, "tensors": w.n, "params": P},
+        "hbm_gbps": round(gbps, 1),
+        "pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "bytes_per_param": path_bytes,
+        "optimizer_step": {"ms": round(opt_ms, 4) if kernels else None,
+                           "params_per_s": P / (opt_ms * 1e-3) if kernels else None,
+                           "GB/s": round(step_bytes * P / (opt_ms * 1e-3) / 1e9, 1) if kernels else None,
+                           "bytes_per_param": step_bytes},
+        "kernels": breakdown,
+        "roofline": roofline,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, device, args.cpu_threads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

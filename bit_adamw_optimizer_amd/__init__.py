@@ -1,0 +1,347 @@
+"""MI355X (gfx950) library for the per-tensor-scaled low-precision AdamW step
+of MS-AMP's O2 and O3 optimization levels, with the per-tensor amax
+reductions and saturating FP8 casts around it.
+
+This module is the thin Python binding of ``libmsamp.so`` (C ABI declared in
+``include/msamp.h``): it only checks tensor arguments and marshals device
+pointers, sizes and the current HIP stream. Every step of the computation runs
+in the library's HIP kernels; there is no fallback. PyTorch provides device
+memory and streams.
+
+Layouts (MS-AMP "Optimization Level" page, sections O2/O3 and the table):
+  O2: grad FP8 (per-tensor scale), exp_avg FP8 E4M3 (own scale), exp_avg_sq
+      FP16, weight FP16.
+  O3: as O2 with the weight replaced by an FP16 master, plus an FP8 E4M3
+      weight copy with its own scale.
+FP8 codes are ``torch.uint8`` tensors (a ``float8_e4m3fn``/``float8_e5m2``
+tensor may be passed, it is read as bytes); FP16 tensors are
+``torch.float16`` (or 16-bit integer views). A meta array is a contiguous
+``float32`` device tensor of shape ``(n, 4)``: ``[amax, scale, scale_inv,
+reserved]`` per tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "MsampError", "TensorList", "lib", "amax", "quantize_fp8",
+    "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "codec_probe", "new_meta",
+    "allocate_state", "state_bytes_per_param", "profile_enable", "profile_read",
+    "KERNELS", "release_cache", "library_path",
+]
+
+E4M3 = 0
+E5M2 = 1
+
+PROBE_F32_TO_E4M3 = 0
+PROBE_F32_TO_E5M2 = 1
+PROBE_E4M3_TO_F32 = 2
+PROBE_E5M2_TO_F32 = 3
+PROBE_F32_TO_F16 = 4
+PROBE_F16_TO_F32 = 5
+
+# kernel kinds of msamp_profile_read, in enum order
+KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
+           "o3_pass3", "finalize", "amax_finalize"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
+
+_STATUS = {0: "MSAMP_OK", 1: "MSAMP_E_INVALID_ARG", 2: "MSAMP_E_MISALIGNED", 3: "MSAMP_E_HIP",
+           4: "MSAMP_E_NO_MEMORY"}
+
+
+class MsampError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libmsamp.so. Raises if it has not been built: there is no
+    other implementation to fall back to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmsamp.so is not built (%s); run __graft_entry__.build() "
+                               "or python -m bit_adamw_optimizer_amd.build" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        st = ctypes.c_int
+        L.msamp_abi_version.argtypes = []
+        L.msamp_abi_version.restype = ctypes.c_int
+        L.msamp_last_error.argtypes = []
+        L.msamp_last_error.restype = ctypes.c_char_p
+        L.msamp_amax.argtypes = [i32, vp, vp, vp, vp]
+        L.msamp_amax.restype = st
+        L.msamp_quantize_fp8.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp]
+        L.msamp_quantize_fp8.restype = st
+        L.msamp_dequantize_fp8.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp]
+        L.msamp_dequantize_fp8.restype = st
+        L.msamp_adamw_o2_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(_HParams), i64, vp]
+        L.msamp_adamw_o2_step.restype = st
+        L.msamp_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(_HParams), i64, vp]
+        L.msamp_adamw_o3_step.restype = st
+        L.msamp_release_cache.argtypes = []
+        L.msamp_release_cache.restype = st
+        L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
+        L.msamp_codec_probe.restype = st
+        L.msamp_profile_enable.argtypes = [ctypes.c_int]
+        L.msamp_profile_enable.restype = st
+        L.msamp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(i64),
+                                         ctypes.POINTER(ctypes.c_double)]
+        L.msamp_profile_read.restype = st
+        L.msamp_kernel_name.argtypes = [ctypes.c_int]
+        L.msamp_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MsampError(status, lib().msamp_last_error().decode())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------ tensor lists ---
+
+_BYTES = {"u8": 1, "f16": 2, "f32": 4}
+
+
+def _role_ok(t: torch.Tensor, kind: str) -> bool:
+    if kind == "u8":
+        return t.element_size() == 1
+    if kind == "f16":
+        return t.dtype in (torch.float16, torch.int16, torch.uint16)
+    if kind == "f32":
+        return t.dtype == torch.float32
+    raise ValueError(kind)
+
+
+class TensorList:
+    """Pointer array and sizes of a list of device tensors, built once.
+
+    An optimizer holds one TensorList per role (grads, exp_avg, ...) for the
+    lifetime of its parameters, so marshalling is not repeated every step.
+    """
+
+    def __init__(self, tensors: Sequence[torch.Tensor], kind: str, name: str = "tensor"):
+        self.tensors = list(tensors)
+        self.kind = kind
+        n = len(self.tensors)
+        self.n = n
+        ptrs = (ctypes.c_void_p * max(n, 1))()
+        numel = (ctypes.c_int64 * max(n, 1))()
+        self.device = None
+        for i, t in enumerate(self.tensors):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError("%s[%d] is not a tensor" % (name, i))
+            if not _role_ok(t, kind):
+                raise TypeError("%s[%d] has dtype %s, expected %s" % (name, i, t.dtype, kind))
+            if not t.is_contiguous():
+                raise ValueError("%s[%d] is not contiguous" % (name, i))
+            if t.device.type != "cuda":
+                raise ValueError("%s[%d] is not on a GPU" % (name, i))
+            if self.device is None:
+                self.device = t.device
+            elif t.device != self.device:
+                raise ValueError("%s[%d] is on %s, expected %s" % (name, i, t.device, self.device))
+            ptrs[i] = t.data_ptr() if t.numel() else 0
+            numel[i] = t.numel()
+        self.ptrs = ptrs
+        self.numel = numel
+        self.sizes = [t.numel() for t in self.tensors]
+
+    def matches(self, other: "TensorList", name: str) -> None:
+        if other.n != self.n or other.sizes != self.sizes:
+            raise ValueError("%s does not match the tensor sizes of the list" % name)
+        if other.n and other.device != self.device:
+            raise ValueError("%s is on another device" % name)
+
+
+def _tl(x, kind: str, name: str) -> TensorList:
+    return x if isinstance(x, TensorList) else TensorList(x, kind, name)
+
+
+def _meta_ptr(meta: torch.Tensor, n: int, device, name: str):
+    if not isinstance(meta, torch.Tensor) or meta.dtype != torch.float32:
+        raise TypeError("%s must be a float32 tensor" % name)
+    if tuple(meta.shape) != (n, 4) or not meta.is_contiguous():
+        raise ValueError("%s must be a contiguous (%d, 4) tensor" % (name, n))
+    if n and meta.device != device:
+        raise ValueError("%s is not on %s" % (name, device))
+    return ctypes.c_void_p(meta.data_ptr() if n else 0)
+
+
+def new_meta(n: int, device) -> torch.Tensor:
+    """Meta array of n tensors in the initial state {amax 0, scale 1,
+    scale_inv 1, 0}."""
+    m = torch.zeros((n, 4), dtype=torch.float32, device=device)
+    m[:, 1] = 1.0
+    m[:, 2] = 1.0
+    return m
+
+
+def _hp(lr, betas, eps, weight_decay) -> _HParams:
+    return _HParams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay))
+
+
+# --------------------------------------------------------------- entry points
+
+def amax(x, meta: torch.Tensor) -> None:
+    """meta[t, 0] <- amax of x[t] (binary32 tensors)."""
+    x = _tl(x, "f32", "x")
+    if x.n == 0:
+        return
+    _check(lib().msamp_amax(x.n, x.ptrs, x.numel, _meta_ptr(meta, x.n, x.device, "meta"),
+                            _stream(x.device)))
+
+
+def quantize_fp8(x, fmt: int, meta: torch.Tensor, q) -> None:
+    """q[t] <- saturating FP8 cast of x[t] * scale(meta[t, 0]); meta[t, 1:3]
+    <- scale, 1/scale."""
+    x = _tl(x, "f32", "x")
+    q = _tl(q, "u8", "q")
+    x.matches(q, "q")
+    if x.n == 0:
+        return
+    _check(lib().msamp_quantize_fp8(x.n, x.ptrs, x.numel, int(fmt),
+                                    _meta_ptr(meta, x.n, x.device, "meta"), q.ptrs,
+                                    _stream(x.device)))
+
+
+def dequantize_fp8(q, fmt: int, meta: torch.Tensor, out) -> None:
+    """out[t] <- decode(q[t]) * meta[t, 2]."""
+    q = _tl(q, "u8", "q")
+    out = _tl(out, "f32", "out")
+    q.matches(out, "out")
+    if q.n == 0:
+        return
+    _check(lib().msamp_dequantize_fp8(q.n, q.ptrs, q.numel, int(fmt),
+                                      _meta_ptr(meta, q.n, q.device, "meta"), out.ptrs,
+                                      _stream(q.device)))
+
+
+def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                  *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int) -> None:
+    """One in-place AdamW step in the O2 layout (see include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    hp = _hp(lr, betas, eps, weight_decay)
+    _check(lib().msamp_adamw_o2_step(
+        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+        ctypes.byref(hp), int(step), _stream(g.device)))
+
+
+def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, master,
+                  weight_fp8, weight_fp8_meta, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
+                  weight_decay=0.01, step: int) -> None:
+    """One in-place AdamW step in the O3 layout (see include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(master, "f16", "master")
+    w8 = _tl(weight_fp8, "u8", "weight_fp8")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "master"), (w8, "weight_fp8")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    hp = _hp(lr, betas, eps, weight_decay)
+    _check(lib().msamp_adamw_o3_step(
+        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+        w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
+        ctypes.byref(hp), int(step), _stream(g.device)))
+
+
+def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:
+    """Element-wise device codec (see msamp_codec_probe)."""
+    if inp.device.type != "cuda" or out.device.type != "cuda":
+        raise ValueError("codec_probe needs device tensors")
+    if inp.numel() != out.numel() or not inp.is_contiguous() or not out.is_contiguous():
+        raise ValueError("codec_probe needs contiguous tensors of equal size")
+    _check(lib().msamp_codec_probe(int(op), ctypes.c_void_p(inp.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), inp.numel(),
+                                   _stream(inp.device)))
+
+
+def release_cache() -> None:
+    _check(lib().msamp_release_cache())
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().msamp_profile_enable(1 if on else 0))
+
+
+def profile_read(kernel: str):
+    """(launches, total milliseconds) recorded for one kernel kind."""
+    kind = KERNELS.index(kernel)
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().msamp_profile_read(kind, ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+# ----------------------------------------------------------- state helpers ---
+
+def allocate_state(weights: Sequence[torch.Tensor], level: str = "O2") -> dict:
+    """Zero-initialized low-precision optimizer state for a list of weights
+    (O2: FP16 weights; O3: FP16 master weights). Returns a dict of tensor
+    lists and meta arrays on the weights' device."""
+    if level not in ("O2", "O3"):
+        raise ValueError("level must be 'O2' or 'O3'")
+    dev = weights[0].device if len(weights) else torch.device("cpu")
+    n = len(weights)
+    st = {
+        "exp_avg": [torch.zeros(w.numel(), dtype=torch.uint8, device=dev) for w in weights],
+        "exp_avg_meta": new_meta(n, dev),
+        "exp_avg_sq": [torch.zeros(w.numel(), dtype=torch.float16, device=dev) for w in weights],
+    }
+    if level == "O3":
+        st["weight_fp8"] = [torch.zeros(w.numel(), dtype=torch.uint8, device=dev) for w in weights]
+        st["weight_fp8_meta"] = new_meta(n, dev)
+    return st
+
+
+def state_bytes_per_param(level: str = "O2") -> dict:
+    """Bytes per parameter of each tensor class in a layout (optimizer
+    states, weight, master, gradient), from the dtypes this library uses."""
+    u8 = torch.tensor([], dtype=torch.uint8).element_size()
+    f16 = torch.tensor([], dtype=torch.float16).element_size()
+    d = {"optimizer_states": u8 + f16, "grad": u8}
+    if level == "O2":
+        d.update(weight=f16, master=0)
+    elif level == "O3":
+        d.update(weight=u8, master=f16)
+    else:
+        raise ValueError(level)
+    return d

@@ -1,0 +1,616 @@
+// abi.hip -- the C ABI declared in include/msamp.h: argument validation,
+// the multi-tensor-apply plan cache (descriptor tables and chunk maps in
+// device memory, keyed on the tensor lists), host-side AdamW constants, the
+// kernel sequence of each entry point, and optional event timing.
+//
+// No C++ exception crosses the interface: every entry point catches and maps
+// failures to a status code with a per-thread message.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kernels.hpp"
+#include "msamp.h"
+
+namespace msamp {
+namespace {
+
+thread_local std::string g_last_error;
+
+msamp_status fail(msamp_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+msamp_status fail_hip(hipError_t e, const char* what) {
+  std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(MSAMP_E_HIP, msg);
+}
+
+// ------------------------------------------------------------ profiler ---
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t get_event() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void recycle_all() {
+    for (auto& r : recs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    recs.clear();
+  }
+};
+
+Profiler& profiler() {
+  static Profiler* p = new Profiler();  // never destroyed: events may outlive static teardown
+  return *p;
+}
+
+// Runs 'launch' (which enqueues one kernel and returns its launch status),
+// bracketed by events when profiling is on.
+template <typename F>
+hipError_t timed(msamp_kernel_kind kind, hipStream_t s, F&& launch) {
+  Profiler& p = profiler();
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(p.mu);
+    on = p.enabled;
+    if (on) {
+      a = p.get_event();
+      b = p.get_event();
+    }
+  }
+  if (on && a && b) (void)hipEventRecord(a, s);
+  hipError_t e = launch();
+  if (on && a && b) {
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(p.mu);
+    p.recs.push_back({(int)kind, a, b});
+  }
+  return e;
+}
+
+// ---------------------------------------------------------- plan cache ---
+
+enum PlanKind : uint64_t { kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3 };
+
+// Device tables of one tensor list: amax scratch (two u32 per tensor, kept
+// at zero between calls), the descriptors and the chunk map, in one
+// allocation uploaded once from pinned host memory.
+struct Plan {
+  int device = -1;
+  std::vector<uint64_t> key;
+  void* dev = nullptr;
+  void* host = nullptr;
+  size_t bytes = 0;
+  uint32_t* scratch_a = nullptr;
+  uint32_t* scratch_b = nullptr;
+  TensorDesc* desc = nullptr;
+  ChunkRef* chunks = nullptr;
+  int64_t nchunks = 0;
+  uint64_t last_use = 0;
+
+  ~Plan() {
+    if (dev) (void)hipFree(dev);
+    if (host) (void)hipHostFree(host);
+  }
+};
+
+struct PlanCache {
+  std::mutex mu;
+  std::unordered_map<uint64_t, std::vector<std::unique_ptr<Plan>>> map;
+  size_t count = 0;
+  size_t bytes = 0;
+  uint64_t tick = 0;
+};
+
+PlanCache& cache() {
+  static PlanCache* c = new PlanCache();
+  return *c;
+}
+
+constexpr size_t kMaxPlans = 64;
+constexpr size_t kMaxPlanBytes = size_t(512) << 20;
+
+uint64_t hash_words(const std::vector<uint64_t>& w) {
+  uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)w.size();
+  for (uint64_t x : w) {
+    h ^= x + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xBF58476D1CE4E5B9ull;
+    h ^= h >> 31;
+  }
+  return h;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Evicts least recently used plans until the cache is within bounds, never
+// the most recently used one (it is being returned to a caller). Waits for
+// the device first: an evicted table may still be read by queued work.
+void evict_locked(PlanCache& c) {
+  while (c.count > kMaxPlans || c.bytes > kMaxPlanBytes) {
+    uint64_t best_tick = UINT64_MAX, best_hash = 0;
+    size_t best_idx = 0;
+    for (auto& kv : c.map)
+      for (size_t i = 0; i < kv.second.size(); ++i)
+        if (kv.second[i]->last_use < best_tick && kv.second[i]->last_use != c.tick) {
+          best_tick = kv.second[i]->last_use;
+          best_hash = kv.first;
+          best_idx = i;
+        }
+    if (best_tick == UINT64_MAX) return;
+    auto& vec = c.map[best_hash];
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(vec[best_idx]->device);
+    (void)hipDeviceSynchronize();
+    c.bytes -= vec[best_idx]->bytes;
+    c.count -= 1;
+    vec.erase(vec.begin() + (ptrdiff_t)best_idx);
+    if (vec.empty()) c.map.erase(best_hash);
+    if (cur >= 0) (void)hipSetDevice(cur);
+  }
+}
+
+// Returns the plan of a tensor list, building and uploading it (on 'stream')
+// the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n);
+// 'min_one_chunk' gives every tensor at least one (possibly empty) chunk.
+msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
+                      const void* const* const* ptrs, int nroles, bool min_one_chunk,
+                      hipStream_t stream, Plan** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+
+  std::vector<uint64_t> key;
+  key.reserve(3 + (size_t)n * (1 + nroles));
+  key.push_back(kind);
+  key.push_back((uint64_t)dev);
+  key.push_back((uint64_t)n);
+  for (int32_t t = 0; t < n; ++t) key.push_back((uint64_t)numel[t]);
+  for (int r = 0; r < nroles; ++r)
+    for (int32_t t = 0; t < n; ++t) key.push_back((uint64_t)(uintptr_t)ptrs[r][t]);
+  const uint64_t h = hash_words(key);
+
+  PlanCache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  auto it = c.map.find(h);
+  if (it != c.map.end()) {
+    for (auto& p : it->second)
+      if (p->key == key) {
+        p->last_use = ++c.tick;
+        *out = p.get();
+        return MSAMP_OK;
+      }
+  }
+
+  // Build the chunk map.
+  std::vector<ChunkRef> chunks;
+  int64_t total = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    int64_t k = (numel[t] + kChunk - 1) / kChunk;
+    if (k == 0 && min_one_chunk) k = 1;
+    if (k > INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "tensor too large for the chunk map");
+    total += k;
+  }
+  if (total > (int64_t)UINT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks");
+  chunks.reserve((size_t)total);
+  for (int32_t t = 0; t < n; ++t) {
+    int64_t k = (numel[t] + kChunk - 1) / kChunk;
+    if (k == 0 && min_one_chunk) k = 1;
+    for (int64_t j = 0; j < k; ++j) chunks.push_back({t, (int32_t)j});
+  }
+
+  auto plan = std::make_unique<Plan>();
+  plan->device = dev;
+  plan->key = std::move(key);
+  const size_t scratch_bytes = align_up(sizeof(uint32_t) * 2 * (size_t)std::max(n, 1), 256);
+  const size_t desc_bytes = align_up(sizeof(TensorDesc) * (size_t)std::max(n, 1), 256);
+  const size_t chunk_bytes = align_up(sizeof(ChunkRef) * std::max<size_t>(chunks.size(), 1), 256);
+  plan->bytes = scratch_bytes + desc_bytes + chunk_bytes;
+
+  e = hipMalloc(&plan->dev, plan->bytes);
+  if (e != hipSuccess) {
+    plan->dev = nullptr;
+    (void)hipGetLastError();
+    return fail(MSAMP_E_NO_MEMORY, "hipMalloc of the descriptor tables failed");
+  }
+  e = hipHostMalloc(&plan->host, plan->bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    plan->host = nullptr;
+    (void)hipGetLastError();
+    return fail(MSAMP_E_NO_MEMORY, "hipHostMalloc of the descriptor staging failed");
+  }
+  char* hb = (char*)plan->host;
+  std::memset(hb, 0, plan->bytes);
+  TensorDesc* hd = (TensorDesc*)(hb + scratch_bytes);
+  for (int32_t t = 0; t < n; ++t) {
+    TensorDesc d;
+    std::memset(&d, 0, sizeof d);
+    d.numel = numel[t];
+    const void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    for (int r = 0; r < nroles && r < 5; ++r) p[r] = ptrs[r][t];
+    d.p0 = p[0];
+    d.p1 = const_cast<void*>(p[1]);
+    d.p2 = const_cast<void*>(p[2]);
+    d.p3 = const_cast<void*>(p[3]);
+    d.p4 = const_cast<void*>(p[4]);
+    hd[t] = d;
+  }
+  if (!chunks.empty())
+    std::memcpy(hb + scratch_bytes + desc_bytes, chunks.data(), chunks.size() * sizeof(ChunkRef));
+
+  char* db = (char*)plan->dev;
+  plan->scratch_a = (uint32_t*)db;
+  plan->scratch_b = (uint32_t*)db + std::max(n, 1);
+  plan->desc = (TensorDesc*)(db + scratch_bytes);
+  plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
+  plan->nchunks = (int64_t)chunks.size();
+
+  e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail_hip(e, "upload of the descriptor tables");
+
+  plan->last_use = ++c.tick;
+  *out = plan.get();
+  c.bytes += plan->bytes;
+  c.count += 1;
+  c.map[h].push_back(std::move(plan));
+  // Never evict the plan just returned: it is the most recently used.
+  evict_locked(c);
+  return MSAMP_OK;
+}
+
+// --------------------------------------------------------- validation ---
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+msamp_status check_list(int32_t n, const int64_t* numel, const void* const* ptrs,
+                        const char* role) {
+  if (ptrs == nullptr) return fail(MSAMP_E_INVALID_ARG, std::string(role) + " array is NULL");
+  for (int32_t t = 0; t < n; ++t) {
+    if (numel[t] == 0) continue;
+    if (ptrs[t] == nullptr)
+      return fail(MSAMP_E_INVALID_ARG,
+                  std::string(role) + "[" + std::to_string(t) + "] is NULL with numel > 0");
+    if (!aligned16(ptrs[t]))
+      return fail(MSAMP_E_MISALIGNED,
+                  std::string(role) + "[" + std::to_string(t) + "] is not 16-byte aligned");
+  }
+  return MSAMP_OK;
+}
+
+msamp_status check_common(int32_t n, const int64_t* numel) {
+  if (n < 0) return fail(MSAMP_E_INVALID_ARG, "n < 0");
+  if (n > 0 && numel == nullptr) return fail(MSAMP_E_INVALID_ARG, "numel array is NULL");
+  for (int32_t t = 0; t < n; ++t)
+    if (numel[t] < 0) return fail(MSAMP_E_INVALID_ARG, "numel[" + std::to_string(t) + "] < 0");
+  return MSAMP_OK;
+}
+
+msamp_status check_fmt(int fmt) {
+  if (fmt != MSAMP_FP8_E4M3 && fmt != MSAMP_FP8_E5M2)
+    return fail(MSAMP_E_INVALID_ARG, "unknown FP8 format");
+  return MSAMP_OK;
+}
+
+msamp_status check_meta(int32_t n, const void* meta, const char* role) {
+  if (n > 0 && meta == nullptr) return fail(MSAMP_E_INVALID_ARG, std::string(role) + " is NULL");
+  if (n > 0 && !aligned16(meta))
+    return fail(MSAMP_E_MISALIGNED, std::string(role) + " is not 16-byte aligned");
+  return MSAMP_OK;
+}
+
+msamp_status check_hparams(const msamp_adamw_hparams* hp, int64_t step) {
+  if (hp == nullptr) return fail(MSAMP_E_INVALID_ARG, "hparams is NULL");
+  if (step < 1) return fail(MSAMP_E_INVALID_ARG, "step must be >= 1");
+  auto fin = [](double x) { return std::isfinite(x); };
+  if (!fin(hp->lr) || hp->lr < 0.0) return fail(MSAMP_E_INVALID_ARG, "lr must be finite and >= 0");
+  if (!fin(hp->beta1) || hp->beta1 < 0.0 || hp->beta1 >= 1.0)
+    return fail(MSAMP_E_INVALID_ARG, "beta1 must be in [0, 1)");
+  if (!fin(hp->beta2) || hp->beta2 < 0.0 || hp->beta2 >= 1.0)
+    return fail(MSAMP_E_INVALID_ARG, "beta2 must be in [0, 1)");
+  if (!fin(hp->eps) || !(hp->eps > 0.0)) return fail(MSAMP_E_INVALID_ARG, "eps must be > 0");
+  if (!fin(hp->weight_decay) || hp->weight_decay < 0.0)
+    return fail(MSAMP_E_INVALID_ARG, "weight_decay must be finite and >= 0");
+  return MSAMP_OK;
+}
+
+// AdamW constants: binary64 expressions, each rounded once to binary32.
+StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step) {
+  const double t = (double)step;
+  const double bc1 = 1.0 - std::pow(hp->beta1, t);
+  const double bc2 = 1.0 - std::pow(hp->beta2, t);
+  StepConsts k;
+  k.b1 = (float)hp->beta1;
+  k.ob1 = (float)(1.0 - hp->beta1);
+  k.b2 = (float)hp->beta2;
+  k.ob2 = (float)(1.0 - hp->beta2);
+  k.eps = (float)hp->eps;
+  k.ss = (float)(hp->lr / bc1);
+  k.ibs = (float)(1.0 / std::sqrt(bc2));
+  k.dec = (float)(1.0 - hp->lr * hp->weight_decay);
+  return k;
+}
+
+#define MSAMP_TRY(expr)                 \
+  do {                                  \
+    msamp_status st__ = (expr);         \
+    if (st__ != MSAMP_OK) return st__;  \
+  } while (0)
+
+#define MSAMP_LAUNCH(kind, stream, call)                                   \
+  do {                                                                     \
+    hipError_t e__ = timed((kind), (stream), [&]() { return (call); });   \
+    if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
+  } while (0)
+
+msamp_status step_impl(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                       int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
+                       msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                       uint16_t* const* weight, uint8_t* const* weight_fp8,
+                       msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp, int64_t step,
+                       void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, o3 ? "master" : "weight"));
+  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
+  if (o3) {
+    MSAMP_TRY(check_list(n, numel, (const void* const*)weight_fp8, "weight_fp8"));
+    MSAMP_TRY(check_meta(n, weight_fp8_meta, "weight_fp8_meta"));
+  }
+  hipStream_t s = (hipStream_t)stream_ptr;
+  const void* const* roles[5] = {(const void* const*)grad, (const void* const*)exp_avg,
+                                 (const void* const*)exp_avg_sq, (const void* const*)weight,
+                                 (const void* const*)weight_fp8};
+  Plan* p = nullptr;
+  MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p));
+  const StepConsts k = make_consts(hp, step);
+
+  MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
+               launch_step_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
+                                 exp_avg_meta, p->scratch_a, k, s));
+  MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
+               launch_step_pass2(grad_fmt, o3, p->desc, p->chunks, p->nchunks, grad_meta,
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s));
+  if (o3)
+    MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+               launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
+                                    o3 ? weight_fp8_meta : nullptr, s));
+  return MSAMP_OK;
+}
+
+template <typename F>
+msamp_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(MSAMP_E_NO_MEMORY, "host allocation failed");
+  } catch (const std::exception& ex) {
+    return fail(MSAMP_E_INVALID_ARG, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MSAMP_E_INVALID_ARG, "internal error");
+  }
+}
+
+}  // namespace
+}  // namespace msamp
+
+using namespace msamp;
+
+extern "C" {
+
+int msamp_abi_version(void) { return MSAMP_ABI_VERSION; }
+
+const char* msamp_last_error(void) { return g_last_error.c_str(); }
+
+const char* msamp_kernel_name(msamp_kernel_kind kind) {
+  switch (kind) {
+    case MSAMP_KERNEL_AMAX: return "amax";
+    case MSAMP_KERNEL_QUANTIZE: return "quantize_fp8";
+    case MSAMP_KERNEL_DEQUANTIZE: return "dequantize_fp8";
+    case MSAMP_KERNEL_STEP_PASS1: return "step_pass1";
+    case MSAMP_KERNEL_O2_PASS2: return "o2_pass2";
+    case MSAMP_KERNEL_O3_PASS2: return "o3_pass2";
+    case MSAMP_KERNEL_O3_PASS3: return "o3_pass3";
+    case MSAMP_KERNEL_FINALIZE: return "finalize";
+    case MSAMP_KERNEL_AMAX_FINALIZE: return "amax_finalize";
+    default: return "";
+  }
+}
+
+msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel, msamp_meta* meta,
+                        void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_common(n, numel));
+    if (n == 0) return MSAMP_OK;
+    MSAMP_TRY(check_list(n, numel, (const void* const*)x, "x"));
+    MSAMP_TRY(check_meta(n, meta, "meta"));
+    hipStream_t s = (hipStream_t)stream;
+    const void* const* roles[1] = {(const void* const*)x};
+    Plan* p = nullptr;
+    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, false, s, &p));
+    MSAMP_LAUNCH(MSAMP_KERNEL_AMAX, s, launch_amax(p->desc, p->chunks, p->nchunks, p->scratch_a, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_AMAX_FINALIZE, s, launch_amax_finalize(n, p->scratch_a, meta, s));
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t* numel,
+                                msamp_fp8_format fmt, msamp_meta* meta, uint8_t* const* q,
+                                void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_common(n, numel));
+    if (n == 0) return MSAMP_OK;
+    MSAMP_TRY(check_fmt((int)fmt));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)x, "x"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)q, "q"));
+    MSAMP_TRY(check_meta(n, meta, "meta"));
+    hipStream_t s = (hipStream_t)stream;
+    const void* const* roles[2] = {(const void* const*)x, (const void* const*)q};
+    Plan* p = nullptr;
+    MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, 2, true, s, &p));
+    MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE, s,
+                 launch_quantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, s));
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int64_t* numel,
+                                  msamp_fp8_format fmt, const msamp_meta* meta,
+                                  float* const* out, void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_common(n, numel));
+    if (n == 0) return MSAMP_OK;
+    MSAMP_TRY(check_fmt((int)fmt));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)q, "q"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)out, "out"));
+    MSAMP_TRY(check_meta(n, meta, "meta"));
+    hipStream_t s = (hipStream_t)stream;
+    const void* const* roles[2] = {(const void* const*)q, (const void* const*)out};
+    Plan* p = nullptr;
+    MSAMP_TRY(get_plan(kPlanDequantize, n, numel, roles, 2, false, s, &p));
+    MSAMP_LAUNCH(MSAMP_KERNEL_DEQUANTIZE, s,
+                 launch_dequantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, s));
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                 msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                 uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                 uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                 const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_impl(false, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                     exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adamw_o3_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                 msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                 uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                 uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                 uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                 const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_impl(true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                     exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, stream);
+  });
+}
+
+msamp_status msamp_release_cache(void) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    PlanCache& c = cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    for (auto& kv : c.map)
+      for (auto& p : kv.second) {
+        (void)hipSetDevice(p->device);
+        (void)hipDeviceSynchronize();
+      }
+    c.map.clear();
+    c.count = 0;
+    c.bytes = 0;
+    if (cur >= 0) (void)hipSetDevice(cur);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int64_t n,
+                               void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    if (n < 0) return fail(MSAMP_E_INVALID_ARG, "n < 0");
+    if ((int)op < 0 || (int)op > (int)MSAMP_PROBE_F16_TO_F32)
+      return fail(MSAMP_E_INVALID_ARG, "unknown probe op");
+    if (n == 0) return MSAMP_OK;
+    if (in == nullptr || out == nullptr) return fail(MSAMP_E_INVALID_ARG, "NULL buffer");
+    if (!aligned16(in) || !aligned16(out)) return fail(MSAMP_E_MISALIGNED, "buffer not 16-byte aligned");
+    hipError_t e = launch_codec_probe((int)op, in, out, n, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "codec probe");
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_profile_enable(int on) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> lk(p.mu);
+    if (on) {
+      // discard earlier records; their events must have completed first
+      for (auto& r : p.recs) (void)hipEventSynchronize(r.b);
+      p.recycle_all();
+    }
+    p.enabled = on != 0;
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_profile_read(msamp_kernel_kind kind, int64_t* launches, double* total_ms) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    if (launches == nullptr || total_ms == nullptr)
+      return fail(MSAMP_E_INVALID_ARG, "NULL output");
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> lk(p.mu);
+    int64_t cnt = 0;
+    double ms = 0.0;
+    for (auto& r : p.recs) {
+      if (r.kind != (int)kind) continue;
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+      float f = 0.0f;
+      e = hipEventElapsedTime(&f, r.a, r.b);
+      if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+      ms += (double)f;
+      ++cnt;
+    }
+    *launches = cnt;
+    *total_ms = ms;
+    return MSAMP_OK;
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// kernels.hpp -- internal interface between the C ABI (abi.hip) and the HIP
+// kernels (kernels.hip). Not installed, not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msamp.h"
+
+namespace msamp {
+
+// Launch geometry. One workgroup of kBlock threads owns one chunk of at most
+// kChunk consecutive elements of one tensor and walks it in tiles of
+// kBlock * kVec elements; each thread handles kVec consecutive elements per
+// tile, so every FP8 stream moves 16 bytes per thread per access and every
+// FP16 stream 2 x 16 bytes.
+constexpr int kBlock = 256;
+constexpr int kVec = 16;
+constexpr int64_t kTile = (int64_t)kBlock * kVec;
+constexpr int64_t kChunk = 16 * kTile;  // 65536 elements
+
+// Multi-tensor-apply descriptor of one tensor (64 bytes). The roles of the
+// pointers depend on the operation:
+//                 p0 (read)     p1            p2           p3          p4
+//   amax          x f32         -             -            -           -
+//   quantize      x f32         q u8 (out)    -            -           -
+//   dequantize    q u8          out f32       -            -           -
+//   O2 step       grad u8       exp_avg u8    exp_avg_sq   weight      -
+//   O3 step       grad u8       exp_avg u8    exp_avg_sq   master      weight_fp8
+struct TensorDesc {
+  const void* p0;
+  void* p1;
+  void* p2;
+  void* p3;
+  void* p4;
+  int64_t numel;
+  int64_t reserved[2];
+};
+static_assert(sizeof(TensorDesc) == 64, "descriptor must stay 64 bytes");
+
+// One workgroup's work item: chunk 'chunk' of tensor 'tensor'.
+struct ChunkRef {
+  int32_t tensor;
+  int32_t chunk;
+};
+
+// AdamW constants of one step (binary64 expressions rounded once).
+struct StepConsts {
+  float b1, ob1, b2, ob2, eps, ss, ibs, dec;
+};
+
+// Every launcher enqueues one kernel on 'stream' and returns the launch
+// status. 'nchunks' workgroups are launched (nothing when 0).
+hipError_t launch_amax(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
+                       uint32_t* scratch, hipStream_t stream);
+hipError_t launch_amax_finalize(int32_t n, uint32_t* scratch, msamp_meta* meta,
+                                hipStream_t stream);
+hipError_t launch_quantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
+                           int64_t nchunks, msamp_meta* meta, hipStream_t stream);
+hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
+                             int64_t nchunks, const msamp_meta* meta, hipStream_t stream);
+hipError_t launch_step_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+                             int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                             uint32_t* amax_m, const StepConsts& k, hipStream_t stream);
+hipError_t launch_step_pass2(int gfmt, bool o3, const TensorDesc* desc, const ChunkRef* chunks,
+                             int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                             const uint32_t* amax_m, uint32_t* amax_w, const StepConsts& k,
+                             hipStream_t stream);
+hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
+                           const uint32_t* amax_w, hipStream_t stream);
+// meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then
+// amax_a[t] <- 0; the same for (amax_b, meta_b) when meta_b is not NULL.
+hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
+                                uint32_t* amax_b, msamp_meta* meta_b, hipStream_t stream);
+hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipStream_t stream);
+
+}  // namespace msamp

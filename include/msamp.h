@@ -1,0 +1,254 @@
+/*
+ * msamp.h -- C ABI of the MI355X (gfx950) library for the per-tensor-scaled
+ * low-precision AdamW step of MS-AMP's O2 and O3 optimization levels, with
+ * the per-tensor amax reductions and saturating FP8 casts around it.
+ *
+ * Sources of the operations (web pages):
+ *   [OL]  MS-AMP docs, "Optimization Level": sections O2 and O3 and the
+ *         optimization-level table (weight gradient FP8; optimizer states
+ *         FP8 + FP16; O2 weight FP16 with no master; O3 weight FP8 with an
+ *         FP16 master weight).
+ *   [RD]  MS-AMP README (giters.com mirror), "Usage": the recognized
+ *         optimizers are torch.optim.Adam and torch.optim.AdamW; "Features":
+ *         memory-limited operations read one byte per element.
+ *   [TE]  TransformerEngine issue #131, "FP8 questions": the two FP8 formats
+ *         E4M3 and E5M2; a cast between precisions is a pass through memory.
+ * The arithmetic the pages leave open is fixed as follows (identical in every
+ * entry point):
+ *   - FP8 formats are the OCP encodings: E4M3 (max 448, no Inf, NaN =
+ *     S.1111.111) and E5M2 (max 57344, IEEE Inf/NaN).
+ *   - Casts to FP8 round to nearest, ties to even, keep subnormals and
+ *     saturate: finite overflow and +-Inf give +-max, NaN gives 0x7F with
+ *     the input's sign bit. Casts to FP16 are IEEE round-to-nearest-even.
+ *   - amax of a tensor is the largest |x| compared as the unsigned integer
+ *     (bits & 0x7FFFFFFF): -0 counts as +0, NaN beats Inf beats finite, an
+ *     empty tensor gives 0.
+ *   - scale = fp8_max / amax, except scale = 1 when amax is 0, Inf or NaN or
+ *     when that quotient is not a finite positive binary32; scale_inv = 1 /
+ *     scale; a code c stands for decode(c) * scale_inv.
+ *   - AdamW is PyTorch's decoupled-weight-decay AdamW in binary32 with the
+ *     new first moment rescaled by its own amax (two passes):
+ *       B1=b1 OB1=1-b1 B2=b2 OB2=1-b2 EPS=eps SS=lr/(1-b1^t)
+ *       IBS=1/sqrt(1-b2^t) DEC=1-lr*wd      (binary64, rounded once)
+ *       g   = decode(g_code) * g_scale_inv
+ *       m0  = decode_e4m3(m_code) * m_scale_inv_old
+ *       m1  = fma(B1, m0, OB1*g)
+ *       v1  = fma(B2, v0, OB2*(g*g))
+ *       den = fma(sqrt(v1), IBS, EPS)
+ *       w1  = fma(-SS, m1/den, w0*DEC)
+ *       m scale from amax(m1); m_code = enc_e4m3(m1*m_scale);
+ *       v = fp16(v1); w = fp16(w1)
+ *     Only the four fma above are fused; every other operation is a
+ *     separately rounded IEEE binary32 operation (division and square root
+ *     correctly rounded).
+ *
+ * Conventions for every entry point:
+ *   - n is the number of tensors (n >= 0; n == 0 is a no-op returning OK).
+ *   - Pointer arrays (x, q, grad, ...) and numel are HOST arrays of length n,
+ *     read only during the call. The pointers they hold are DEVICE pointers
+ *     to contiguous, flat 1-D arrays with a 16-byte aligned base.
+ *   - Meta arrays are DEVICE arrays of n msamp_meta records.
+ *   - A tensor with numel == 0 may have NULL pointers.
+ *   - stream is a hipStream_t (NULL = the null stream). All work is enqueued
+ *     on it; nothing synchronizes the host. Inputs must stay alive and
+ *     unmodified until that work completes.
+ *   - The caller owns every tensor and meta array. The library owns cached
+ *     device tables (tensor descriptors, chunk maps, amax scratch) keyed on
+ *     the pointer lists; msamp_release_cache() frees them.
+ *   - Calls that use the same tensor lists must be ordered (same stream, or
+ *     synchronized): they share that list's amax scratch.
+ *   - Errors: every argument is validated before anything is enqueued; on an
+ *     error nothing is enqueued and a status other than MSAMP_OK is returned,
+ *     with a description from msamp_last_error() (per thread). No C++
+ *     exception crosses this interface. Faults inside kernels surface at the
+ *     caller's next synchronization.
+ *   - Different roles must not alias (e.g. exp_avg and weight); this is not
+ *     checked.
+ */
+#ifndef MSAMP_H_
+#define MSAMP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSAMP_ABI_VERSION 1
+
+typedef enum {
+  MSAMP_OK = 0,
+  MSAMP_E_INVALID_ARG = 1, /* bad count, NULL pointer, bad format or hyperparameter */
+  MSAMP_E_MISALIGNED = 2,  /* a tensor base is not 16-byte aligned */
+  MSAMP_E_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  MSAMP_E_NO_MEMORY = 4    /* the library could not allocate its tables */
+} msamp_status;
+
+typedef enum {
+  MSAMP_FP8_E4M3 = 0, /* OCP E4M3, max 448 */
+  MSAMP_FP8_E5M2 = 1  /* OCP E5M2, max 57344 */
+} msamp_fp8_format;
+
+/* Per-tensor scaling record (16 bytes). */
+typedef struct {
+  float amax;      /* largest |x| of the tensor it describes */
+  float scale;     /* fp8_max / amax (see the scale rule above) */
+  float scale_inv; /* 1 / scale: value = decode(code) * scale_inv */
+  float reserved;  /* written as 0 by the library */
+} msamp_meta;
+
+/* AdamW hyperparameters (PyTorch's torch.optim.AdamW meaning, [RD] "Usage").
+ * Valid: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps > 0, weight_decay >= 0,
+ * all finite. */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+} msamp_adamw_hparams;
+
+/* Version of this interface (MSAMP_ABI_VERSION). */
+int msamp_abi_version(void);
+
+/* Description of the last error of the calling thread ("" if none). */
+const char* msamp_last_error(void);
+
+/*
+ * msamp_amax -- per-tensor amax of binary32 tensors ([OL] per-tensor scaled
+ * FP8 gradients; [TE] "a pass through memory").
+ *   x[t]      device float[numel[t]]
+ *   meta[t]   device; .amax is written, the other fields are left unchanged
+ * Reads 4 bytes per element.
+ */
+msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel,
+                        msamp_meta* meta, void* stream);
+
+/*
+ * msamp_quantize_fp8 -- saturating FP8 cast of binary32 tensors with their
+ * per-tensor scale ([OL] FP8 weight gradient; [TE] E4M3/E5M2).
+ *   x[t]      device float[numel[t]]
+ *   meta[t]   device; .amax is READ (normally written by msamp_amax; a
+ *             smaller caller value saturates the outliers), .scale and
+ *             .scale_inv are written, .reserved is written as 0
+ *   q[t]      device uint8[numel[t]]: enc(x * scale)
+ * Reads 4 and writes 1 byte per element.
+ */
+msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t* numel,
+                                msamp_fp8_format fmt, msamp_meta* meta, uint8_t* const* q,
+                                void* stream);
+
+/*
+ * msamp_dequantize_fp8 -- out = decode(q) * meta.scale_inv (binary32).
+ *   q[t]      device uint8[numel[t]]
+ *   meta[t]   device, read
+ *   out[t]    device float[numel[t]]
+ */
+msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int64_t* numel,
+                                  msamp_fp8_format fmt, const msamp_meta* meta,
+                                  float* const* out, void* stream);
+
+/*
+ * msamp_adamw_o2_step -- one AdamW step in the O2 layout ([OL] section O2
+ * and table row "MS-AMP O2": weight FP16, no master, gradient FP8,
+ * optimizer states FP8 + FP16), in place.
+ *   numel[t]          host, elements of tensor t
+ *   grad[t]           device uint8 FP8 codes in grad_fmt, read
+ *   grad_meta[t]      device, read (.scale_inv)
+ *   exp_avg[t]        device uint8 E4M3 codes of the first moment, in/out
+ *   exp_avg_meta[t]   device, in (.scale_inv of the stored codes) / out
+ *                     ({amax, scale, scale_inv} of the new codes)
+ *   exp_avg_sq[t]     device binary16 bits of the second moment, in/out
+ *   weight[t]         device binary16 bits of the weight, in/out
+ *   hp                host hyperparameters
+ *   step              1-based step count after increment (t >= 1); the
+ *                     library keeps no step state
+ * Initial state: exp_avg codes 0, exp_avg_meta {0, 1, 1, 0}, exp_avg_sq 0.
+ * Two passes: 13 bytes per element (read g, m; then read g, m, v, w and
+ * write m, v, w). Non-finite gradient codes are outside the contract (the
+ * caller skips such steps, as GradScaler does in [RD] "Usage").
+ */
+msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                 msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                 uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                 uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                 const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
+/*
+ * msamp_adamw_o3_step -- one AdamW step in the O3 layout ([OL] section O3
+ * and table row "MS-AMP O3": FP16 master weight, FP8 regular weight), in
+ * place. Arguments as msamp_adamw_o2_step, with the FP16 weight replaced by
+ *   master[t]           device binary16 bits of the master weight, in/out
+ *   weight_fp8[t]       device uint8 E4M3 codes, out: enc(master * s_w)
+ *                       taken from the stored (rounded) new master
+ *   weight_fp8_meta[t]  device, out: {amax_w, s_w, 1/s_w, 0}, amax_w over
+ *                       the new master
+ * Three passes: 16 bytes per element.
+ */
+msamp_status msamp_adamw_o3_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                 msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                 uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                 uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                 uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                 const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
+/* Frees every cached device table of the library (all devices) after
+ * waiting for the devices to finish. Safe to call at any time from one
+ * thread while no other library call runs. */
+msamp_status msamp_release_cache(void);
+
+/* ----------------------------------------------------------------------
+ * Test- and measurement-facing entry points.
+ * ---------------------------------------------------------------------- */
+
+/* Element-wise device codec used by every kernel above, exposed so that it
+ * can be compared with an independent codec on every input of interest:
+ *   MSAMP_PROBE_F32_TO_E4M3 / _E5M2  in float[n]    -> out uint8[n] (unscaled
+ *                                    saturating cast)
+ *   MSAMP_PROBE_E4M3_TO_F32 / _E5M2  in uint8[n]    -> out float[n]
+ *   MSAMP_PROBE_F32_TO_F16           in float[n]    -> out uint16[n]
+ *   MSAMP_PROBE_F16_TO_F32           in uint16[n]   -> out float[n]
+ * in/out are device pointers, 16-byte aligned; n >= 0. */
+typedef enum {
+  MSAMP_PROBE_F32_TO_E4M3 = 0,
+  MSAMP_PROBE_F32_TO_E5M2 = 1,
+  MSAMP_PROBE_E4M3_TO_F32 = 2,
+  MSAMP_PROBE_E5M2_TO_F32 = 3,
+  MSAMP_PROBE_F32_TO_F16 = 4,
+  MSAMP_PROBE_F16_TO_F32 = 5
+} msamp_probe_op;
+
+msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int64_t n,
+                               void* stream);
+
+/* Kernel timing with HIP events recorded on the launch stream around every
+ * kernel the library enqueues (off by default). */
+typedef enum {
+  MSAMP_KERNEL_AMAX = 0,        /* msamp_amax reduction */
+  MSAMP_KERNEL_QUANTIZE = 1,    /* msamp_quantize_fp8 */
+  MSAMP_KERNEL_DEQUANTIZE = 2,  /* msamp_dequantize_fp8 */
+  MSAMP_KERNEL_STEP_PASS1 = 3,  /* first-moment amax pass (O2 and O3) */
+  MSAMP_KERNEL_O2_PASS2 = 4,    /* O2 update pass */
+  MSAMP_KERNEL_O3_PASS2 = 5,    /* O3 update pass (+ master amax) */
+  MSAMP_KERNEL_O3_PASS3 = 6,    /* O3 FP8 weight copy */
+  MSAMP_KERNEL_FINALIZE = 7,    /* per-tensor meta write-back of a step */
+  MSAMP_KERNEL_AMAX_FINALIZE = 8, /* amax write-back of msamp_amax */
+  MSAMP_KERNEL_COUNT = 9
+} msamp_kernel_kind;
+
+/* on != 0 starts recording (and discards earlier records); on == 0 stops. */
+msamp_status msamp_profile_enable(int on);
+
+/* Waits for the recorded events and returns, for one kernel kind, the number
+ * of launches and the summed duration in milliseconds since the last
+ * msamp_profile_enable(1). */
+msamp_status msamp_profile_read(msamp_kernel_kind kind, int64_t* launches, double* total_ms);
+
+/* Name of a kernel kind (static string; "" for an unknown kind). */
+const char* msamp_kernel_name(msamp_kernel_kind kind);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MSAMP_H_ */

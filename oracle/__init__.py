@@ -235,7 +235,9 @@ class TensorState:
             self.w8_meta = np.array([0.0, 1.0, 1.0, 0.0], np.float32)
 
 
-def _one_tensor_step(state: TensorState, grad_f32: np.ndarray, gfmt: int, step: int, hp: dict):
+def step_tensor(state: TensorState, grad_f32: np.ndarray, gfmt: int, step: int, **hp):
+    """Gradient amax + quantize, then one O2/O3 step of one tensor's state.
+    Returns the gradient (codes, meta)."""
     qg, gmeta = quantize_fp8(grad_f32, gfmt)
     if state.level == "O2":
         adamw_o2_tensor(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.w, step, **hp)
@@ -249,7 +251,7 @@ def step_list(states, grads_f32, gfmt: int, step: int, threads: int = 1, **hp):
     """Grad amax + quantize + one O2/O3 step for every tensor of a list.
     Returns the per-tensor (codes, meta) of the quantized gradients."""
     if threads <= 1:
-        return [_one_tensor_step(s, g, gfmt, step, hp) for s, g in zip(states, grads_f32)]
+        return [step_tensor(s, g, gfmt, step, **hp) for s, g in zip(states, grads_f32)]
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        futs = [ex.submit(_one_tensor_step, s, g, gfmt, step, hp) for s, g in zip(states, grads_f32)]
+        futs = [ex.submit(step_tensor, s, g, gfmt, step, **hp) for s, g in zip(states, grads_f32)]
         return [f.result() for f in futs]

@@ -1,0 +1,132 @@
+"""msamp_amax / msamp_quantize_fp8 / msamp_dequantize_fp8 through the C ABI
+against the oracle: bit-exact amax, scales and codes from identical binary32
+inputs, on tensor lists with empty, tiny and ragged tensors (several chunks
+and a partial last tile), special values and caller-supplied amax.
+Per-tensor scaled FP8 gradients: MS-AMP optimization-level table (weight
+gradient FP8); formats: TransformerEngine issue #131."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adamw_optimizer_amd as M
+import oracle as O
+from tests.parity import log, u32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# empty, tiny, ragged, exactly one tile/chunk, multi-chunk with ragged tail
+SIZES = [0, 1, 2, 15, 16, 17, 255, 4095, 4096, 4097, 65535, 65536, 65537, 3 * 65536 + 4099, 1_000_003]
+
+
+def _tensors(rng, sizes, specials=True):
+    out = []
+    for k in sizes:
+        x = (rng.standard_t(3, k) * 10.0 ** rng.uniform(-6, 2)).astype(np.float32)
+        if specials and k > 8:
+            idx = rng.choice(k, 6, replace=False)
+            x[idx] = np.array([0.0, -0.0, 1e-40, -1e-45, 3e-39, -5e-42], np.float32)
+        out.append(x)
+    return out
+
+
+def _to_dev(xs):
+    return [torch.from_numpy(x).to(DEV) for x in xs]
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_amax_quantize_dequantize_bit_exact(fmt):
+    log("amax/quantize fmt=%d" % fmt)
+    rng = np.random.default_rng(100 + fmt)
+    xs = _tensors(rng, SIZES)
+    # an all-zero tensor and a single-element tensor
+    xs += [np.zeros(777, np.float32), np.array([-3.25e-3], np.float32)]
+    dx = _to_dev(xs)
+    n = len(xs)
+    meta = M.new_meta(n, DEV)
+    meta[:, 3] = 7.0  # reserved is rewritten by quantize
+    q = [torch.full((x.size,), 0xAB, dtype=torch.uint8, device=DEV) for x in xs]
+    M.amax(dx, meta)
+    torch.cuda.synchronize()
+    m_after_amax = meta.cpu().numpy()
+    M.quantize_fp8(dx, fmt, meta, q)
+    out = [torch.full((x.size,), float("nan"), dtype=torch.float32, device=DEV) for x in xs]
+    M.dequantize_fp8(q, fmt, meta, out)
+    torch.cuda.synchronize()
+    mg = meta.cpu().numpy()
+    for t, x in enumerate(xs):
+        a = O.amax(x)
+        assert u32(m_after_amax[t, 0]) == u32(a), t
+        # amax leaves scale / scale_inv untouched
+        assert m_after_amax[t, 1] == 1.0 and m_after_amax[t, 2] == 1.0
+        qr, mr = O.quantize_fp8(x, fmt)
+        assert np.array_equal(u32(mg[t, :3]), u32(mr[:3])), (t, mg[t], mr)
+        assert mg[t, 3] == 0.0
+        qq = q[t].cpu().numpy()
+        bad = np.nonzero(qq != qr)[0]
+        assert bad.size == 0, (t, x.size, bad[:5], qq[bad[:5]], qr[bad[:5]])
+        dr = O.dequantize_fp8(qr, fmt, mr[2])
+        assert np.array_equal(out[t].cpu().numpy().view(np.uint32), dr.view(np.uint32)), t
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_nan_inf_and_caller_amax(fmt):
+    log("specials fmt=%d" % fmt)
+    rng = np.random.default_rng(7)
+    a = (rng.standard_normal(5000) * 1e-3).astype(np.float32)
+    b = a.copy()
+    b[[3, 4000]] = [np.inf, -np.inf]
+    c = a.copy()
+    c[[10, 11, 4999]] = [np.nan, -np.inf, -np.nan]
+    xs = [a, b, c, a.copy()]
+    dx = _to_dev(xs)
+    meta = M.new_meta(4, DEV)
+    M.amax(dx, meta)
+    torch.cuda.synchronize()
+    m0 = meta.cpu().numpy()
+    assert np.isposinf(m0[1, 0]) and np.isnan(m0[2, 0])
+    # caller-supplied amax below the true one for the last tensor: saturation
+    meta[3, 0] = float(O.amax(a)) / 16
+    q = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for x in xs]
+    M.quantize_fp8(dx, fmt, meta, q)
+    torch.cuda.synchronize()
+    mg = meta.cpu().numpy()
+    for t, x in enumerate(xs):
+        amax_in = np.float32(mg[t, 0])
+        qr, mr = O.quantize_fp8(x, fmt, amax_value=amax_in)
+        assert np.array_equal(u32(mg[t, :3]), u32(mr[:3])), t
+        assert np.array_equal(q[t].cpu().numpy(), qr), t
+
+
+def test_amax_permutation_invariant_and_deterministic():
+    log("amax permutation")
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(2_000_001) * 1e-2).astype(np.float32)
+    perms = [x, rng.permutation(x), rng.permutation(x)]
+    meta = M.new_meta(3, DEV)
+    M.amax(_to_dev(perms), meta)
+    torch.cuda.synchronize()
+    m = meta.cpu().numpy()
+    assert u32(m[0, 0]) == u32(m[1, 0]) == u32(m[2, 0]) == u32(O.amax(x))
+
+
+def test_misaligned_and_invalid_arguments_enqueue_nothing():
+    log("abi errors")
+    base = torch.zeros(1024, dtype=torch.float32, device=DEV)
+    meta = M.new_meta(1, DEV)
+    before = meta.clone()
+    with pytest.raises(M.MsampError) as e:
+        M.amax([base[1:]], meta)  # 4-byte offset: not 16-byte aligned
+    assert e.value.status == 2
+    q = torch.zeros(1023, dtype=torch.uint8, device=DEV)
+    with pytest.raises(M.MsampError) as e:
+        M.quantize_fp8([base[1:]], 0, meta, [q])
+    assert e.value.status == 2
+    with pytest.raises(M.MsampError) as e:
+        M.quantize_fp8([base], 7, meta, [torch.zeros(1024, dtype=torch.uint8, device=DEV)])
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.equal(meta, before)
+    # n = 0 is a no-op
+    M.amax([], M.new_meta(0, DEV))

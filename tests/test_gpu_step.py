@@ -1,0 +1,152 @@
+"""The O2 and O3 AdamW steps through the C ABI against the oracle, at sizes
+the oracle finishes in seconds: independent trajectories over the steps of
+each workload, gradient codes and scales bit-exact, optimizer outputs at the
+bar (>= 99.99% identical, the rest within 1 ulp). Layouts: MS-AMP
+"Optimization Level" page, sections O2 and O3 and the table."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adamw_optimizer_amd as M
+import oracle as O
+from bit_adamw_optimizer_amd import workloads as W
+from tests.parity import GpuState, assert_bar, host, log, run_parity, u32
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, stats):
+    log("%s: " % name + ", ".join("%s %.6f/%dulp" % (k, s.frac, s.max_ulp)
+                                  for k, s in stats.items() if s.total))
+
+
+def test_single_1m_o2_10_steps():
+    w = W.make("single_1m")
+    log("single_1m O2, %d params, 10 steps" % w.params)
+    stats, _, _ = run_parity(w, 10)
+    _report("single_1m", stats)
+    assert_bar(stats)
+
+
+def test_tiny_llama_o2_10_steps():
+    w = W.make("tiny_llama")
+    log("tiny_llama O2, %d tensors, %d params" % (w.n, w.params))
+    stats, _, _ = run_parity(w, 10)
+    _report("tiny_llama", stats)
+    assert_bar(stats)
+
+
+def test_tiny_llama_o3_10_steps():
+    w = W.make("tiny_llama_o3")
+    log("tiny_llama O3, %d tensors, %d params" % (w.n, w.params))
+    stats, _, _ = run_parity(w, 10)
+    _report("tiny_llama_o3", stats)
+    assert_bar(stats)
+
+
+def test_tiny_stress_e5m2_10_steps():
+    w = W.make("tiny_stress")
+    log("tiny_stress O2 E5M2, %d tensors, %d params, %d zero" % (w.n, w.params, len(w.zero_tensors)))
+    stats, gs, ost = run_parity(w, 10)
+    _report("tiny_stress", stats)
+    assert_bar(stats)
+    # all-zero gradient tensors keep zero moments and scale 1
+    mm = gs.exp_avg_meta.cpu().numpy()
+    for t in w.zero_tensors:
+        assert (host(gs.exp_avg[t]) == 0).all()
+        assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
+
+
+def test_ragged_sizes_o2_and_o3():
+    """Sizes around the 16-element vector, the 4096-element tile and the
+    65536-element chunk, including empty tensors."""
+    sizes = [0, 1, 7, 15, 16, 17, 31, 4095, 4096, 4097, 65535, 65536, 65537, 131072 + 4096 + 9, 0, 3]
+    for level in ("O2", "O3"):
+        w = W.Workload("ragged_" + level, level, W.E4M3, 4, ["t%d" % i for i in range(len(sizes))],
+                       sizes, lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.05, seed_base=11)
+        log("ragged %s" % level)
+        stats, gs, _ = run_parity(w, 4)
+        _report(w.name, stats)
+        assert_bar(stats)
+        mm = gs.exp_avg_meta.cpu().numpy()
+        for t, k in enumerate(sizes):
+            if k == 0:
+                assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
+
+
+def test_gpt2_small_o2_10_steps():
+    w = W.make("gpt2_small")
+    log("gpt2_small O2, %d tensors, %d params" % (w.n, w.params))
+    stats, _, _ = run_parity(w, 10)
+    _report("gpt2_small", stats)
+    assert_bar(stats)
+
+
+def test_deterministic_and_resume_bit_exact():
+    """Two runs from the same state are bit-identical, and 3 steps + a
+    save/restore of the whole state + 3 steps equals 6 straight steps."""
+    w = W.make("tiny_llama_o3")
+    log("determinism / resume")
+
+    def snapshot(gs):
+        return [t.clone() for t in gs.exp_avg + gs.exp_avg_sq + gs.weights + gs.weight_fp8] + \
+            [gs.exp_avg_meta.clone(), gs.weight_fp8_meta.clone()]
+
+    a = GpuState(w, "cuda")
+    b = GpuState(w, "cuda")
+    for s in range(1, 4):
+        for gs in (a, b):
+            gs.fill_grads(s)
+            gs.step(s)
+    torch.cuda.synchronize()
+    sa, sb = snapshot(a), snapshot(b)
+    assert all(torch.equal(x, y) for x, y in zip(sa, sb))
+    # save to host, clobber, restore
+    saved = [t.cpu() for t in snapshot(b)]
+    for t in b.exp_avg + b.exp_avg_sq + b.weights + b.weight_fp8:
+        t.fill_(0)
+    live = b.exp_avg + b.exp_avg_sq + b.weights + b.weight_fp8 + [b.exp_avg_meta, b.weight_fp8_meta]
+    for dst, src in zip(live, saved):
+        dst.copy_(src)
+    for s in range(4, 7):
+        for gs in (a, b):
+            gs.fill_grads(s)
+            gs.step(s)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(snapshot(a), snapshot(b)))
+
+
+def test_o3_weight_copy_overwrites_every_element_and_max_code():
+    w = W.Workload("cover", "O3", W.E4M3, 1, ["a", "b", "c"], [4097, 65537, 33], seed_base=12)
+    gs = GpuState(w, "cuda")
+    for t in gs.weight_fp8:
+        t.fill_(0x7F)  # NaN code: never produced by the step
+    gs.fill_grads(1)
+    gs.step(1)
+    torch.cuda.synchronize()
+    for t in range(w.n):
+        w8 = host(gs.weight_fp8[t])
+        assert not (w8 == 0x7F).any() and not (w8 == 0xFF).any()
+        assert (w8 & 0x7F).max() == 0x7E
+        assert (host(gs.exp_avg[t]) & 0x7F).max() == 0x7E
+
+
+def test_step_argument_errors():
+    w = W.Workload("err", "O2", W.E4M3, 1, ["a"], [100], seed_base=13)
+    gs = GpuState(w, "cuda")
+    before = gs.weights[0].clone()
+    hp = w.hparams()
+    for bad in (dict(step=0), dict(step=1, eps=0.0), dict(step=1, betas=(1.0, 0.999)),
+                dict(step=1, lr=float("nan"))):
+        kw = dict(hp)
+        kw.update(bad)
+        with pytest.raises(M.MsampError) as e:
+            M.adamw_o2_step(gs.tl_gq, 0, gs.grad_meta, gs.tl_m, gs.exp_avg_meta, gs.tl_v, gs.tl_w, **kw)
+        assert e.value.status == 1
+    shifted = torch.zeros(101, dtype=torch.uint8, device="cuda")[1:]  # 1-byte offset
+    with pytest.raises(M.MsampError) as e:
+        M.adamw_o2_step(gs.tl_gq, 0, gs.grad_meta, [shifted], gs.exp_avg_meta,
+                        gs.tl_v, gs.tl_w, step=1, **hp)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.equal(before, gs.weights[0])
