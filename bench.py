@@ -90,20 +90,22 @@ class State:
         from bit_adamw_optimizer_amd import workloads as W
 
         self.w = w
-        self.weights = W.init_weights(w, device)
-        st = M.allocate_state(self.weights, w.level)
+        # every role lives in one allocation (views per tensor)
+        self.weights = W.init_weights(w, device, out=M.flat_views(w.numel, torch.float16, device))
+        st = M.allocate_state(self.weights, w.level, flat=True)
         self.exp_avg_meta = st["exp_avg_meta"]
         self.weight_fp8_meta = st.get("weight_fp8_meta")
         self.tl_m = M.TensorList(st["exp_avg"], "u8", "exp_avg")
         self.tl_v = M.TensorList(st["exp_avg_sq"], "f16", "exp_avg_sq")
         self.tl_w = M.TensorList(self.weights, "f16", "weight")
         self.tl_w8 = M.TensorList(st["weight_fp8"], "u8", "weight_fp8") if w.level == "O3" else None
-        self.grad_q = M.TensorList([torch.empty(k, dtype=torch.uint8, device=device) for k in w.numel],
-                                   "u8", "grad_q")
+        self.grad_q = M.TensorList(M.flat_views(w.numel, torch.uint8, device), "u8", "grad_q")
         self.grad_meta = M.new_meta(w.n, device)
         self.grad_sets = []
         for s in (1, 2):
-            g = [W.grad_tensor(w, t, s, device) for t in range(w.n)]
+            g = M.flat_views(w.numel, torch.float32, device)
+            for t in range(w.n):
+                W.grad_tensor(w, t, s, device, out=g[t])
             self.grad_sets.append(M.TensorList(g, "f32", "grad_f32"))
         torch.cuda.synchronize()
 

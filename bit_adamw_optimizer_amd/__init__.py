@@ -30,7 +30,7 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "MsampError", "TensorList", "lib", "amax", "quantize_fp8",
     "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "codec_probe", "new_meta",
-    "allocate_state", "state_bytes_per_param", "profile_enable", "profile_read",
+    "allocate_state", "flat_views", "state_bytes_per_param", "profile_enable", "profile_read",
     "KERNELS", "release_cache", "library_path",
 ]
 
@@ -313,21 +313,43 @@ def profile_read(kernel: str):
 
 # ----------------------------------------------------------- state helpers ---
 
-def allocate_state(weights: Sequence[torch.Tensor], level: str = "O2") -> dict:
+# Views into one allocation start at multiples of this many elements, which
+# keeps every view 16-byte aligned for 1-, 2- and 4-byte element types.
+FLAT_ALIGN = 16
+
+
+def flat_views(sizes: Sequence[int], dtype, device, fill=0):
+    """One contiguous allocation holding len(sizes) tensors, returned as 1-D
+    views (each starting at a multiple of FLAT_ALIGN elements). On MI355X one
+    large buffer per role streams faster than many separate allocations."""
+    offsets, total = [], 0
+    for k in sizes:
+        offsets.append(total)
+        total += -(-int(k) // FLAT_ALIGN) * FLAT_ALIGN
+    buf = torch.full((max(total, 1),), fill, dtype=dtype, device=device)
+    return [buf[o:o + int(k)] for o, k in zip(offsets, sizes)]
+
+
+def allocate_state(weights: Sequence[torch.Tensor], level: str = "O2", flat: bool = True) -> dict:
     """Zero-initialized low-precision optimizer state for a list of weights
     (O2: FP16 weights; O3: FP16 master weights). Returns a dict of tensor
-    lists and meta arrays on the weights' device."""
+    lists and meta arrays on the weights' device. With flat=True each role
+    lives in one allocation (see flat_views)."""
     if level not in ("O2", "O3"):
         raise ValueError("level must be 'O2' or 'O3'")
     dev = weights[0].device if len(weights) else torch.device("cpu")
     n = len(weights)
-    st = {
-        "exp_avg": [torch.zeros(w.numel(), dtype=torch.uint8, device=dev) for w in weights],
-        "exp_avg_meta": new_meta(n, dev),
-        "exp_avg_sq": [torch.zeros(w.numel(), dtype=torch.float16, device=dev) for w in weights],
-    }
+    sizes = [w.numel() for w in weights]
+
+    def zeros(dtype):
+        if flat:
+            return flat_views(sizes, dtype, dev)
+        return [torch.zeros(k, dtype=dtype, device=dev) for k in sizes]
+
+    st = {"exp_avg": zeros(torch.uint8), "exp_avg_meta": new_meta(n, dev),
+          "exp_avg_sq": zeros(torch.float16)}
     if level == "O3":
-        st["weight_fp8"] = [torch.zeros(w.numel(), dtype=torch.uint8, device=dev) for w in weights]
+        st["weight_fp8"] = zeros(torch.uint8)
         st["weight_fp8_meta"] = new_meta(n, dev)
     return st
 

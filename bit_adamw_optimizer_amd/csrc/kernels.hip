@@ -5,11 +5,16 @@
 //
 // All kernels are multi-tensor-apply launches: workgroup b takes ChunkRef b
 // (tensor t, chunk j) and covers elements [j*kChunk, min(numel, (j+1)*kChunk))
-// of tensor t through the 64-byte TensorDesc of t. Inside a chunk every
-// thread owns kVec = 16 consecutive elements per tile, so the FP8 streams are
-// moved with one 16-byte access per thread, the FP16 streams with two and
-// the FP32 streams with four; a ragged end of a tensor is handled element by
-// element. The work is bound by HBM bandwidth: no matrix cores are involved.
+// of tensor t through the 64-byte TensorDesc of t, in tiles of 4096
+// elements (4 waves x 1024). Inside a wave's 1024 elements the lanes are laid
+// out so that every load and store instruction of the wave covers one
+// contiguous span of memory:
+//   FP8 / FP16 streams: lane l owns the 8-element groups at l*8 and
+//     512 + l*8 (one 8-byte FP8 access or one 16-byte FP16 access per group)
+//   FP32 streams: lane l owns the 4-element groups at k*256 + l*4, k = 0..3
+//     (one 16-byte access per group)
+// A ragged end of a tensor is handled element by element. The work is bound
+// by HBM bandwidth; no matrix cores are involved.
 //
 // Arithmetic is binary32 with the operation order of the AdamW definition in
 // msamp.h; the file is compiled with -ffp-contract=off so that only the
@@ -25,12 +30,53 @@ namespace {
 
 constexpr float kE4M3Max = 448.0f;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Tensor pointers come from the descriptor table as generic pointers; they
+// are global memory, and saying so lets the compiler use global (not flat)
+// memory instructions.
+#define GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ GLOBAL T* global_ptr(void* p) {
+  return (GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ const GLOBAL T* global_ptr(const void* p) {
+  return (const GLOBAL T*)p;
+}
+
+// Streams that are read once and not written back are loaded non-temporally
+// (they need not stay in the caches).
+template <typename T>
+__device__ __forceinline__ T load_stream(const GLOBAL void* p) {
+  return __builtin_nontemporal_load((const GLOBAL T*)p);
+}
+template <typename T>
+__device__ __forceinline__ T load(const GLOBAL void* p) {
+  return *(const GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void store(GLOBAL void* p, T v) {
+  *(GLOBAL T*)p = v;
+}
+// Write-only output streams (nothing reads them back in the same kernel) are
+// stored non-temporally; on MI355X this lowers the cost of the writes.
+template <typename T>
+__device__ __forceinline__ void store_stream(GLOBAL void* p, T v) {
+  __builtin_nontemporal_store(v, (GLOBAL T*)p);
+}
+
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Largest value of the workgroup, folded into *dst with one atomic max (only
-// when it is nonzero: the destination starts at 0).
+// Largest value of the workgroup, folded into *dst with one atomic max. The
+// destination starts at 0 and only grows, so the atomic is skipped when the
+// value already there is at least as large: every workgroup of a tensor
+// targets the same word, and without this check ~10^5 same-address atomics
+// per launch serialize at one L2 channel.
 __device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
   __shared__ uint32_t partial[kBlock / 64];
 #pragma unroll
@@ -43,7 +89,8 @@ __device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
     uint32_t m = partial[0];
 #pragma unroll
     for (int k = 1; k < kBlock / 64; ++k) m = umax(m, partial[k]);
-    if (m != 0u) atomicMax(dst, m);
+    if (m != 0u && m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, m);
   }
 }
 
@@ -53,22 +100,30 @@ __device__ __forceinline__ float dec1(uint8_t code) {
   return dec_pair<FMT, false>((uint32_t)code).x;
 }
 
+// Eight FP8 codes (two words) to binary32.
 template <int FMT>
-__device__ __forceinline__ void dec16(const uint4& q, float* f) {
+__device__ __forceinline__ void dec8(const u32x2& q, float* f) {
   dec4<FMT>(q.x, f);
   dec4<FMT>(q.y, f + 4);
-  dec4<FMT>(q.z, f + 8);
-  dec4<FMT>(q.w, f + 12);
 }
 
-__device__ __forceinline__ void h8_to_f8(const uint4& h, float* f) {
+// Eight binary32 values to FP8 codes (finite inputs, saturating).
+template <int FMT>
+__device__ __forceinline__ u32x2 enc8(const float* f) {
+  u32x2 r;
+  r.x = enc4<FMT>(f);
+  r.y = enc4<FMT>(f + 4);
+  return r;
+}
+
+__device__ __forceinline__ void h8_to_f8(const u32x4& h, float* f) {
   f32x2 a = h2_to_f2(h.x), b = h2_to_f2(h.y), c = h2_to_f2(h.z), d = h2_to_f2(h.w);
   f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
   f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
 }
 
-__device__ __forceinline__ uint4 f8_to_h8(const float* f) {
-  uint4 r;
+__device__ __forceinline__ u32x4 f8_to_h8(const float* f) {
+  u32x4 r;
   r.x = f2_to_h2(f[0], f[1]);
   r.y = f2_to_h2(f[2], f[3]);
   r.z = f2_to_h2(f[4], f[5]);
@@ -96,24 +151,39 @@ __device__ __forceinline__ ChunkRange chunk_range(const ChunkRef* chunks, const 
   return r;
 }
 
+// First element of this lane's 8-element groups (FP8/FP16 layout) in the
+// tile starting at 'tile': e0 and e0 + 512.
+__device__ __forceinline__ int64_t group8_base(int64_t tile) {
+  return tile + (threadIdx.x >> 6) * 1024 + (threadIdx.x & 63) * 8;
+}
+
+// First element of this lane's 4-element group k (FP32 layout).
+__device__ __forceinline__ int64_t group4_base(int64_t tile, int k) {
+  return tile + (threadIdx.x >> 6) * 1024 + k * 256 + (threadIdx.x & 63) * 4;
+}
+
 // ---------------------------------------------------------------- amax ---
 
 __global__ __launch_bounds__(kBlock) void k_amax(const TensorDesc* __restrict__ desc,
                                                  const ChunkRef* __restrict__ chunks,
                                                  uint32_t* __restrict__ scratch) {
   const ChunkRange r = chunk_range(chunks, desc);
-  const float* __restrict__ x = (const float*)desc[r.t].p0;
+  const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].p0);
   uint32_t m = 0u;
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
-      const uint4* p = (const uint4*)(x + i);
-      uint4 a = p[0], b = p[1], c = p[2], d = p[3];
-      uint32_t u[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w,
-                        c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    if (group4_base(tile, 3) + 4 <= r.end) {
+      u32x4 v[4];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) m = umax(m, u[k] & 0x7FFFFFFFu);
+      for (int k = 0; k < 4; ++k) v[k] = load_stream<u32x4>(x + group4_base(tile, k));
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m = umax(m, umax(umax(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu),
+                         umax(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu)));
     } else {
-      for (int64_t e = i; e < r.end; ++e) m = umax(m, abs_bits(x[e]));
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = group4_base(tile, k);
+        for (int64_t i = e; i < e + 4 && i < r.end; ++i) m = umax(m, abs_bits(x[i]));
+      }
     }
   }
   block_max_into(m, &scratch[r.t]);
@@ -140,22 +210,24 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const TensorDesc* __restric
     meta[r.t].scale_inv = 1.0f / s;
     meta[r.t].reserved = 0.0f;
   }
-  const float* __restrict__ x = (const float*)desc[r.t].p0;
-  uint8_t* __restrict__ q = (uint8_t*)desc[r.t].p1;
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
-      const float4* p = (const float4*)(x + i);
-      float4 a = p[0], b = p[1], c = p[2], d = p[3];
-      float f[16] = {a.x * s, a.y * s, a.z * s, a.w * s, b.x * s, b.y * s, b.z * s, b.w * s,
-                     c.x * s, c.y * s, c.z * s, c.w * s, d.x * s, d.y * s, d.z * s, d.w * s};
-      uint4 o;
-      o.x = enc4_nan<FMT>(f);
-      o.y = enc4_nan<FMT>(f + 4);
-      o.z = enc4_nan<FMT>(f + 8);
-      o.w = enc4_nan<FMT>(f + 12);
-      *(uint4*)(q + i) = o;
+  const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].p0);
+  GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(desc[r.t].p1);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    if (group4_base(tile, 3) + 4 <= r.end) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = load_stream<u32x4>(x + group4_base(tile, k));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float f[4] = {__uint_as_float(v[k].x) * s, __uint_as_float(v[k].y) * s,
+                      __uint_as_float(v[k].z) * s, __uint_as_float(v[k].w) * s};
+        store_stream<uint32_t>(q + group4_base(tile, k), enc4_nan<FMT>(f));
+      }
     } else {
-      for (int64_t e = i; e < r.end; ++e) q[e] = (uint8_t)enc1_nan<FMT>(x[e] * s);
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = group4_base(tile, k);
+        for (int64_t i = e; i < e + 4 && i < r.end; ++i) q[i] = (uint8_t)enc1_nan<FMT>(x[i] * s);
+      }
     }
   }
 }
@@ -166,18 +238,27 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const TensorDesc* __restr
                                                        const msamp_meta* __restrict__ meta) {
   const ChunkRange r = chunk_range(chunks, desc);
   const float si = meta[r.t].scale_inv;
-  const uint8_t* __restrict__ q = (const uint8_t*)desc[r.t].p0;
-  float* __restrict__ out = (float*)desc[r.t].p1;
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
-      float f[16];
-      dec16<FMT>(*(const uint4*)(q + i), f);
-      float4* o = (float4*)(out + i);
+  const GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(desc[r.t].p0);
+  GLOBAL float* __restrict__ out = global_ptr<float>(desc[r.t].p1);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    if (group4_base(tile, 3) + 4 <= r.end) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = make_float4(f[4 * k] * si, f[4 * k + 1] * si, f[4 * k + 2] * si, f[4 * k + 3] * si);
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = group4_base(tile, k);
+        float f[4];
+        dec4<FMT>(load<uint32_t>(q + e), f);
+        u32x4 o;
+        o.x = __float_as_uint(f[0] * si);
+        o.y = __float_as_uint(f[1] * si);
+        o.z = __float_as_uint(f[2] * si);
+        o.w = __float_as_uint(f[3] * si);
+        store<u32x4>(out + e, o);
+      }
     } else {
-      for (int64_t e = i; e < r.end; ++e) out[e] = dec1<FMT>(q[e]) * si;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t e = group4_base(tile, k);
+        for (int64_t i = e; i < e + 4 && i < r.end; ++i) out[i] = dec1<FMT>(q[i]) * si;
+      }
     }
   }
 }
@@ -209,23 +290,26 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   const ChunkRange r = chunk_range(chunks, desc);
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
-  const uint8_t* __restrict__ gq = (const uint8_t*)desc[r.t].p0;
-  const uint8_t* __restrict__ mq = (const uint8_t*)desc[r.t].p1;
+  const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
+  const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
   uint32_t mx = 0u;
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
+      const u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
+      const u32x2 M0 = load<u32x2>(mq + e0), M1 = load<u32x2>(mq + e1);
       float g[16], m[16];
-      dec16<GF>(*(const uint4*)(gq + i), g);
-      dec16<kE4M3>(*(const uint4*)(mq + i), m);
+      dec8<GF>(G0, g);
+      dec8<GF>(G1, g + 8);
+      dec8<kE4M3>(M0, m);
+      dec8<kE4M3>(M1, m + 8);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float m1 = first_moment(k, g[e] * gsi, m[e] * msi);
-        mx = umax(mx, abs_bits(m1));
-      }
+      for (int e = 0; e < 16; ++e) mx = umax(mx, abs_bits(first_moment(k, g[e] * gsi, m[e] * msi)));
     } else {
-      for (int64_t e = i; e < r.end; ++e) {
-        const float m1 = first_moment(k, dec1<GF>(gq[e]) * gsi, dec1<kE4M3>(mq[e]) * msi);
-        mx = umax(mx, abs_bits(m1));
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i)
+          mx = umax(mx, abs_bits(first_moment(k, dec1<GF>(gq[i]) * gsi, dec1<kE4M3>(mq[i]) * msi)));
       }
     }
   }
@@ -247,22 +331,23 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
   const float s_m = scale_rule(__uint_as_float(amax_m[r.t]), kE4M3Max);
-  const uint8_t* __restrict__ gq = (const uint8_t*)desc[r.t].p0;
-  uint8_t* __restrict__ mq = (uint8_t*)desc[r.t].p1;
-  uint16_t* __restrict__ vh = (uint16_t*)desc[r.t].p2;
-  uint16_t* __restrict__ wh = (uint16_t*)desc[r.t].p3;
+  const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
+  GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
+  GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   uint32_t wmax = 0u;  // FP16 magnitude bits of the new weight (O3)
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
-      const uint4 G = *(const uint4*)(gq + i);
-      const uint4 M = *(const uint4*)(mq + i);
-      const uint4 V0 = *(const uint4*)(vh + i);
-      const uint4 V1 = *(const uint4*)(vh + i + 8);
-      const uint4 W0 = *(const uint4*)(wh + i);
-      const uint4 W1 = *(const uint4*)(wh + i + 8);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
+      const u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
+      const u32x2 M0 = load<u32x2>(mq + e0), M1 = load<u32x2>(mq + e1);
+      const u32x4 V0 = load<u32x4>(vh + e0), V1 = load<u32x4>(vh + e1);
+      const u32x4 W0 = load<u32x4>(wh + e0), W1 = load<u32x4>(wh + e1);
       float g[16], m[16], v[16], w[16];
-      dec16<GF>(G, g);
-      dec16<kE4M3>(M, m);
+      dec8<GF>(G0, g);
+      dec8<GF>(G1, g + 8);
+      dec8<kE4M3>(M0, m);
+      dec8<kE4M3>(M1, m + 8);
       h8_to_f8(V0, v);
       h8_to_f8(V1, v + 8);
       h8_to_f8(W0, w);
@@ -277,18 +362,13 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
         v[e] = v1;
         w[e] = w1;
       }
-      uint4 Mo;
-      Mo.x = enc4<kE4M3>(m);
-      Mo.y = enc4<kE4M3>(m + 4);
-      Mo.z = enc4<kE4M3>(m + 8);
-      Mo.w = enc4<kE4M3>(m + 12);
-      const uint4 Vo0 = f8_to_h8(v), Vo1 = f8_to_h8(v + 8);
-      const uint4 Wo0 = f8_to_h8(w), Wo1 = f8_to_h8(w + 8);
-      *(uint4*)(mq + i) = Mo;
-      *(uint4*)(vh + i) = Vo0;
-      *(uint4*)(vh + i + 8) = Vo1;
-      *(uint4*)(wh + i) = Wo0;
-      *(uint4*)(wh + i + 8) = Wo1;
+      const u32x4 Wo0 = f8_to_h8(w), Wo1 = f8_to_h8(w + 8);
+      store<u32x2>(mq + e0, enc8<kE4M3>(m));
+      store<u32x2>(mq + e1, enc8<kE4M3>(m + 8));
+      store<u32x4>(vh + e0, f8_to_h8(v));
+      store<u32x4>(vh + e1, f8_to_h8(v + 8));
+      store<u32x4>(wh + e0, Wo0);
+      store<u32x4>(wh + e1, Wo1);
       if (O3) {
         const uint32_t ws[8] = {Wo0.x, Wo0.y, Wo0.z, Wo0.w, Wo1.x, Wo1.y, Wo1.z, Wo1.w};
 #pragma unroll
@@ -296,17 +376,20 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
           wmax = umax(wmax, umax(ws[k2] & 0x7FFFu, (ws[k2] >> 16) & 0x7FFFu));
       }
     } else {
-      for (int64_t e = i; e < r.end; ++e) {
-        const float ge = dec1<GF>(gq[e]) * gsi;
-        const float m1 = first_moment(k, ge, dec1<kE4M3>(mq[e]) * msi);
-        float v1, w1;
-        second_moment_and_weight(k, ge, m1, h_to_f(vh[e]), h_to_f(wh[e]), v1, w1);
-        float mm[4] = {m1 * s_m, 0.0f, 0.0f, 0.0f};
-        mq[e] = (uint8_t)(enc4<kE4M3>(mm) & 0xFFu);
-        vh[e] = f_to_h(v1);
-        const uint16_t wn = f_to_h(w1);
-        wh[e] = wn;
-        if (O3) wmax = umax(wmax, (uint32_t)(wn & 0x7FFFu));
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          const float ge = dec1<GF>(gq[i]) * gsi;
+          const float m1 = first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi);
+          float v1, w1;
+          second_moment_and_weight(k, ge, m1, h_to_f(vh[i]), h_to_f(wh[i]), v1, w1);
+          float mm[4] = {m1 * s_m, 0.0f, 0.0f, 0.0f};
+          mq[i] = (uint8_t)(enc4<kE4M3>(mm) & 0xFFu);
+          vh[i] = f_to_h(v1);
+          const uint16_t wn = f_to_h(w1);
+          wh[i] = wn;
+          if (O3) wmax = umax(wmax, (uint32_t)(wn & 0x7FFFu));
+        }
       }
     }
   }
@@ -324,25 +407,25 @@ __global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restric
                                                      const uint32_t* __restrict__ amax_w) {
   const ChunkRange r = chunk_range(chunks, desc);
   const float s_w = scale_rule(__uint_as_float(amax_w[r.t]), kE4M3Max);
-  const uint16_t* __restrict__ wh = (const uint16_t*)desc[r.t].p3;
-  uint8_t* __restrict__ w8 = (uint8_t*)desc[r.t].p4;
-  for (int64_t i = r.begin + (int64_t)threadIdx.x * kVec; i < r.end; i += kTile) {
-    if (i + kVec <= r.end) {
+  const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
+  GLOBAL uint8_t* __restrict__ w8 = global_ptr<uint8_t>(desc[r.t].p4);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
       float w[16];
-      h8_to_f8(*(const uint4*)(wh + i), w);
-      h8_to_f8(*(const uint4*)(wh + i + 8), w + 8);
+      h8_to_f8(load_stream<u32x4>(wh + e0), w);
+      h8_to_f8(load_stream<u32x4>(wh + e1), w + 8);
 #pragma unroll
       for (int e = 0; e < 16; ++e) w[e] = w[e] * s_w;
-      uint4 o;
-      o.x = enc4<kE4M3>(w);
-      o.y = enc4<kE4M3>(w + 4);
-      o.z = enc4<kE4M3>(w + 8);
-      o.w = enc4<kE4M3>(w + 12);
-      *(uint4*)(w8 + i) = o;
+      store_stream<u32x2>(w8 + e0, enc8<kE4M3>(w));
+      store_stream<u32x2>(w8 + e1, enc8<kE4M3>(w + 8));
     } else {
-      for (int64_t e = i; e < r.end; ++e) {
-        float ww[4] = {h_to_f(wh[e]) * s_w, 0.0f, 0.0f, 0.0f};
-        w8[e] = (uint8_t)(enc4<kE4M3>(ww) & 0xFFu);
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          float ww[4] = {h_to_f(wh[i]) * s_w, 0.0f, 0.0f, 0.0f};
+          w8[i] = (uint8_t)(enc4<kE4M3>(ww) & 0xFFu);
+        }
       }
     }
   }

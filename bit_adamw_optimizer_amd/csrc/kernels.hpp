@@ -9,14 +9,11 @@
 
 namespace msamp {
 
-// Launch geometry. One workgroup of kBlock threads owns one chunk of at most
-// kChunk consecutive elements of one tensor and walks it in tiles of
-// kBlock * kVec elements; each thread handles kVec consecutive elements per
-// tile, so every FP8 stream moves 16 bytes per thread per access and every
-// FP16 stream 2 x 16 bytes.
+// Launch geometry. One workgroup of kBlock threads (4 waves) owns one chunk
+// of at most kChunk consecutive elements of one tensor and walks it in tiles
+// of kTile elements, 16 per thread and 1024 per wave.
 constexpr int kBlock = 256;
-constexpr int kVec = 16;
-constexpr int64_t kTile = (int64_t)kBlock * kVec;
+constexpr int64_t kTile = (int64_t)kBlock * 16;
 constexpr int64_t kChunk = 16 * kTile;  // 65536 elements
 
 // Multi-tensor-apply descriptor of one tensor (64 bytes). The roles of the

@@ -176,14 +176,20 @@ def _gen(device, seed: int) -> torch.Generator:
     return g
 
 
-def init_weights(w: Workload, device) -> List[torch.Tensor]:
-    """FP16 weights (O3: master weights) = fp16(0.02 * N(0, 1)), per tensor."""
-    out = []
+def init_weights(w: Workload, device, out: Optional[List[torch.Tensor]] = None) -> List[torch.Tensor]:
+    """FP16 weights (O3: master weights) = fp16(0.02 * N(0, 1)), per tensor;
+    written into 'out' (a list of FP16 tensors of the right sizes) if given."""
+    res = []
     for t, k in enumerate(w.numel):
         x = torch.randn(k, generator=_gen(device, w.tensor_seed(t, 0)), device=device,
                         dtype=torch.float32)
-        out.append((x * 0.02).to(torch.float16))
-    return out
+        h = (x * 0.02).to(torch.float16)
+        if out is not None:
+            out[t].copy_(h)
+            res.append(out[t])
+        else:
+            res.append(h)
+    return res
 
 
 def grad_tensor(w: Workload, t: int, step: int, device, out: Optional[torch.Tensor] = None):
