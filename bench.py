@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,6 +65,10 @@ def parse():
                    help="do not bracket kernels with HIP events")
     p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                    help="only run a device-to-device copy of this many GiB (counter calibration)")
+    p.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR",
+                                                            "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="write profiles/ summaries from rocprofv3 CSV output directories "
+                        "(no GPU needed)")
     return p.parse_args()
 
 
@@ -153,6 +158,134 @@ def cpu_baseline(w, device, threads: int) -> dict:
                                                          sub.params, w.level)}
 
 
+# rocprofv3 kernel names of the library's kernels -> profile kernel kinds
+KERNEL_SYMBOLS = {"k_amax(": "amax", "k_quantize<": "quantize_fp8", "k_step_pass1<": "step_pass1",
+                  "k_step_pass2<0, false>": "o2_pass2", "k_step_pass2<1, false>": "o2_pass2",
+                  "k_step_pass2<0, true>": "o3_pass2", "k_step_pass2<1, true>": "o3_pass2",
+                  "k_o3_pass3(": "o3_pass3"}
+
+
+def _kind_of(name: str):
+    for sym, kind in KERNEL_SYMBOLS.items():
+        if "msamp::" in name and sym in name:
+            return kind
+    return None
+
+
+def summarize_profiles(dirs, workload: str) -> None:
+    """Summaries of rocprofv3 runs for profiles/: the kernel-trace statistics
+    of the library's kernels, and per-launch HBM bytes from FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the same counter reads for a plain copy of
+    a known size (--calibrate-copy)."""
+    import csv
+    import glob
+
+    trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+
+    def one(pattern):
+        files = glob.glob(os.path.join(pattern, "**", "*.csv"), recursive=True)
+        return files
+
+    stats = [f for f in one(trace_dir) if f.endswith("_kernel_stats.csv")]
+    rows = list(csv.DictReader(open(stats[0]))) if stats else []
+
+    def counters(d, name):
+        files = [f for f in one(d) if f.endswith("_counter_collection.csv")]
+        agg = {}
+        for r in csv.DictReader(open(files[0])):
+            if r["Counter_Name"] != name:
+                continue
+            agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return agg
+
+    def copy_kib(d, name):
+        agg = counters(d, name)
+        vals = [v for k, vs in agg.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs]
+        return max(vals)  # the one big calibration copy
+
+    def source_hash(d):
+        for f in glob.glob(os.path.join(os.path.dirname(d.rstrip("/")), "*.log")) + \
+                glob.glob(os.path.join(os.path.dirname(d.rstrip("/")), "*.json")):
+            for line in open(f, errors="replace"):
+                if line.startswith("{") and "kernel_source_hash" in line:
+                    return json.loads(line)["kernel_source_hash"]
+        return None
+
+    copy_bytes = None
+    for f in glob.glob(os.path.join(os.path.dirname(cfetch_dir.rstrip("/")), "*.log")):
+        for line in open(f, errors="replace"):
+            if line.startswith("{") and "calibrate_copy_bytes_read" in line:
+                copy_bytes = json.loads(line)["calibrate_copy_bytes_read"]
+    assert copy_bytes, "no calibration copy output found"
+    ffac = copy_bytes / (copy_kib(cfetch_dir, "FETCH_SIZE") * 1024.0)
+    wfac = copy_bytes / (copy_kib(cwrite_dir, "WRITE_SIZE") * 1024.0)
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+    h = source_hash(fetch_dir)
+
+    from bit_adamw_optimizer_amd import workloads as W
+    w = W.make(workload)
+    per_param = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES, "step_pass1": PASS1_BYTES,
+                 "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES, "o3_pass3": PASS3_BYTES}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = ["# HBM traffic per launch, %s (%d params), from rocprofv3 counters" % (workload, w.params), "",
+             "Commands (run from the repository root; R=$PWD; cd /tmp first):",
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_fetch -o fetch -- python3 $R/bench.py "
+             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile" % workload,
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_write -o write -- python3 $R/bench.py "
+             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile" % workload,
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_copy_fetch -o cfetch -- python3 "
+             "$R/bench.py --calibrate-copy 4",
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_copy_write -o cwrite -- python3 "
+             "$R/bench.py --calibrate-copy 4",
+             "  python bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/pmc_fetch "
+             "gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write --workload %s" % workload,
+             "",
+             "Calibration: a %d-byte device copy reads FETCH_SIZE x %.4f and WRITE_SIZE x %.4f bytes;"
+             " these factors scale the counters below." % (copy_bytes, ffac, wfac),
+             "Kernel sources hash: %s" % h, "",
+             "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    out = {}
+    for name in sorted(set(fetch) | set(write)):
+        kind = _kind_of(name)
+        if kind is None:
+            continue
+        f = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [0])))
+        wr = sum(write.get(name, [0])) / max(1, len(write.get(name, [0])))
+        hbm = f * 1024 * ffac + wr * 1024 * wfac
+        alg = per_param[kind] * w.params
+        out[kind] = {"fetch_kib": f, "write_kib": wr, "hbm_bytes_per_launch": hbm, "algorithmic_bytes": alg}
+        lines.append("| %s | %d | %.1f | %.1f | %.4g | %.4g | %.4f |"
+                     % (kind, len(fetch.get(name, [])), f, wr, hbm, alg, hbm / alg))
+    with open(os.path.join(ROOT, "profiles", "path_kernels_%s_hbm_counters.md" % workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    for kind, d in out.items():
+        d.update({"kernel": kind, "workload": workload, "kernel_source_hash": h,
+                  "fetch_factor": ffac, "write_factor": wfac})
+        with open(os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kind, workload)), "w") as fh:
+            json.dump(d, fh, indent=1)
+    if rows:
+        tl = ["# rocprofv3 kernel-trace statistics, %s (%d params)" % (workload, w.params), "",
+              "Command (run from the repository root; R=$PWD; cd /tmp first):",
+              "  rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o o2_7b -- python3 "
+              "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline" % workload, "",
+              "| kernel | calls | average ms | min ms | max ms | algorithmic GB/s (avg) |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            kind = _kind_of(r["Name"])
+            if kind is None and "msamp::" not in r["Name"]:
+                continue
+            avg = float(r["AverageNs"]) * 1e-6
+            gbps = per_param[kind] * w.params / (avg * 1e-3) / 1e9 if kind in per_param else float("nan")
+            m = re.search(r"\b(k_\w+)", r["Name"])
+            short = kind or (m.group(1) if m else r["Name"][:40])
+            tl.append("| %s | %s | %.4f | %.4f | %.4f | %.1f |" % (short, r["Calls"], avg,
+                      float(r["MinNs"]) * 1e-6, float(r["MaxNs"]) * 1e-6, gbps))
+        with open(os.path.join(ROOT, "profiles", "path_kernels_%s_kernel_trace.md" % workload), "w") as fh:
+            fh.write("\n".join(tl) + "\n")
+    print("wrote profiles for %s" % workload)
+
+
 def traffic_from_profiles(kernel: str, workload: str, params: int):
     """HBM bytes per launch from committed counter runs, when they were taken
     on the current kernel sources (else None)."""
@@ -170,6 +303,9 @@ def traffic_from_profiles(kernel: str, workload: str, params: int):
 
 def main() -> int:
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
