@@ -85,11 +85,11 @@ def lib():
         L.oracle_dequantize_fp8.restype = i32
         L.oracle_adamw_constants.argtypes = [hp, i64, vp]
         L.oracle_adamw_constants.restype = None
-        L.oracle_adamw_f32_tensor.argtypes = [i64, vp, vp, vp, vp, hp, i64]
+        L.oracle_adamw_f32_tensor.argtypes = [i64, vp, vp, vp, vp, hp, i64, i32]
         L.oracle_adamw_f32_tensor.restype = None
-        L.oracle_adamw_o2_tensor.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, hp, i64]
+        L.oracle_adamw_o2_tensor.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, hp, i64, i32]
         L.oracle_adamw_o2_tensor.restype = i32
-        L.oracle_adamw_o3_tensor.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, hp, i64]
+        L.oracle_adamw_o3_tensor.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, vp, vp, hp, i64, i32]
         L.oracle_adamw_o3_tensor.restype = i32
         _lib = L
     return _lib
@@ -175,37 +175,41 @@ def dequantize_fp8(q, fmt: int, scale_inv) -> np.ndarray:
 # ---------------------------------------------------------------- AdamW ---
 
 def adamw_constants(step: int, **hp) -> np.ndarray:
-    """[B1, OB1, B2, OB2, EPS, SS, IBS, DEC] as float32."""
-    k = np.zeros(8, np.float32)
+    """[B1, OB1, B2, OB2, EPS, SS, IBS, DEC, WD] as float32."""
+    k = np.zeros(9, np.float32)
     h = _hp(**hp)
     lib().oracle_adamw_constants(ctypes.byref(h), int(step), _ptr(k))
     return k
 
 
-def adamw_f32_tensor(g, m, v, w, step: int, **hp) -> None:
-    """AdamW with binary32 states, in place on m, v, w (float32 arrays)."""
+def adamw_f32_tensor(g, m, v, w, step: int, adam: bool = False, **hp) -> None:
+    """AdamW (adam=True: Adam with coupled L2) with binary32 states, in place
+    on m, v, w (float32 arrays)."""
     for a in (m, v, w):
         assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"]
     g = np.ascontiguousarray(g, dtype=np.float32)
     h = _hp(**hp)
-    lib().oracle_adamw_f32_tensor(g.size, _ptr(g), _ptr(m), _ptr(v), _ptr(w), ctypes.byref(h), int(step))
+    lib().oracle_adamw_f32_tensor(g.size, _ptr(g), _ptr(m), _ptr(v), _ptr(w), ctypes.byref(h),
+                                  int(step), int(bool(adam)))
 
 
-def adamw_o2_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, w, step: int, **hp) -> None:
+def adamw_o2_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, w, step: int, adam: bool = False,
+                    **hp) -> None:
     """One O2 step on one tensor, in place on qm (uint8), m_meta (float32[4]),
-    v and w (uint16 FP16 bits)."""
+    v and w (uint16 FP16 bits). adam=True: Adam (coupled L2) instead of AdamW."""
     assert qm.dtype == np.uint8 and v.dtype == np.uint16 and w.dtype == np.uint16
     assert m_meta.dtype == np.float32 and m_meta.size >= 3
     qg = np.ascontiguousarray(qg, dtype=np.uint8)
     h = _hp(**hp)
     rc = lib().oracle_adamw_o2_tensor(qg.size, _ptr(qg), gfmt, float(np.float32(g_scale_inv)),
                                       _ptr(qm), _ptr(m_meta), _ptr(v), _ptr(w), ctypes.byref(h),
-                                      int(step))
+                                      int(step), int(bool(adam)))
     if rc != 0:
         raise RuntimeError("oracle_adamw_o2_tensor failed (%d)" % rc)
 
 
-def adamw_o3_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, master, w8, w8_meta, step: int, **hp) -> None:
+def adamw_o3_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, master, w8, w8_meta, step: int,
+                    adam: bool = False, **hp) -> None:
     """One O3 step on one tensor, in place on qm, m_meta, v, master (FP16
     bits), w8 (uint8 E4M3) and w8_meta (float32[4])."""
     assert master.dtype == np.uint16 and w8.dtype == np.uint8 and w8_meta.dtype == np.float32
@@ -213,7 +217,7 @@ def adamw_o3_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, master, w8, w8_meta, s
     h = _hp(**hp)
     rc = lib().oracle_adamw_o3_tensor(qg.size, _ptr(qg), gfmt, float(np.float32(g_scale_inv)),
                                       _ptr(qm), _ptr(m_meta), _ptr(v), _ptr(master), _ptr(w8),
-                                      _ptr(w8_meta), ctypes.byref(h), int(step))
+                                      _ptr(w8_meta), ctypes.byref(h), int(step), int(bool(adam)))
     if rc != 0:
         raise RuntimeError("oracle_adamw_o3_tensor failed (%d)" % rc)
 
@@ -223,9 +227,10 @@ def adamw_o3_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, master, w8, w8_meta, s
 class TensorState:
     """Host copy of one tensor's low-precision optimizer state."""
 
-    def __init__(self, weight_f16_bits: np.ndarray, level: str = "O2"):
+    def __init__(self, weight_f16_bits: np.ndarray, level: str = "O2", adam: bool = False):
         n = weight_f16_bits.size
         self.level = level
+        self.adam = adam  # Adam with coupled L2 instead of AdamW
         self.w = np.ascontiguousarray(weight_f16_bits, dtype=np.uint16).copy()  # weight or master
         self.m = np.zeros(n, np.uint8)
         self.m_meta = np.array([0.0, 1.0, 1.0, 0.0], np.float32)
@@ -240,10 +245,11 @@ def step_tensor(state: TensorState, grad_f32: np.ndarray, gfmt: int, step: int, 
     Returns the gradient (codes, meta)."""
     qg, gmeta = quantize_fp8(grad_f32, gfmt)
     if state.level == "O2":
-        adamw_o2_tensor(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.w, step, **hp)
+        adamw_o2_tensor(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.w, step,
+                        adam=state.adam, **hp)
     else:
         adamw_o3_tensor(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.w, state.w8,
-                        state.w8_meta, step, **hp)
+                        state.w8_meta, step, adam=state.adam, **hp)
     return qg, gmeta
 
 

@@ -44,6 +44,11 @@
  *             to +-Inf.
  *   R-O3COPY  the FP8 regular weight of O3 is taken from the stored (rounded)
  *             FP16 master, E4M3, with the same scale rule.
+ *   R-ADAM    torch.optim.Adam (the other optimizer the README recognizes)
+ *             applies weight decay as an L2 term added to the gradient before
+ *             the moments: gd = fma(WD, w0, g) with WD = (float)wd, then the
+ *             AdamW formulas above with gd in place of g and DEC = 1 (no
+ *             decoupled decay; w0*1 is exact).
  *
  * Build: a C11 compiler with -O2 -ffp-contract=off (no fast-math), so that
  * only the four fmaf calls above are fused and every other operation is a
@@ -297,7 +302,7 @@ typedef struct {
   double lr, beta1, beta2, eps, weight_decay;
 } oracle_hparams;
 
-enum { K_B1 = 0, K_OB1, K_B2, K_OB2, K_EPS, K_SS, K_IBS, K_DEC, K_COUNT };
+enum { K_B1 = 0, K_OB1, K_B2, K_OB2, K_EPS, K_SS, K_IBS, K_DEC, K_WD, K_COUNT };
 
 /* Per-step constants, computed in binary64 and rounded once to binary32.
  * 'step' is the 1-based step count after increment. */
@@ -313,7 +318,17 @@ void oracle_adamw_constants(const oracle_hparams* hp, int64_t step, float* k) {
   k[K_SS] = (float)(hp->lr / bc1);
   k[K_IBS] = (float)(1.0 / sqrt(bc2));
   k[K_DEC] = (float)(1.0 - hp->lr * hp->weight_decay);
+  k[K_WD] = (float)hp->weight_decay;
 }
+
+/* The gradient the moments see. AdamW: g. Adam (coupled L2, R-ADAM):
+ * g + wd*w0 with one fused multiply-add. */
+static float effective_grad(const float* k, int coupled, float g, float w0) {
+  return coupled ? fmaf(k[K_WD], w0, g) : g;
+}
+
+/* Decay factor of the update: 1 - lr*wd for AdamW, 1 for Adam. */
+static float decay_factor(const float* k, int coupled) { return coupled ? 1.0f : k[K_DEC]; }
 
 /* First moment: m1 = beta1*m0 + (1-beta1)*g, one fused multiply-add. */
 static float adamw_first_moment(const float* k, float g, float m0) {
@@ -324,25 +339,28 @@ static float adamw_first_moment(const float* k, float g, float m0) {
  *   v1  = beta2*v0 + (1-beta2)*g^2
  *   den = sqrt(v1)/sqrt(1-beta2^t) + eps
  *   w1  = w0*(1-lr*wd) - (lr/(1-beta1^t)) * m1/den                          */
-static void adamw_second_moment_and_weight(const float* k, float g, float m1, float v0, float w0,
-                                           float* v1_out, float* w1_out) {
+static void adamw_second_moment_and_weight(const float* k, float dec, float g, float m1, float v0,
+                                           float w0, float* v1_out, float* w1_out) {
   float v1 = fmaf(k[K_B2], v0, k[K_OB2] * (g * g));
   float den = fmaf(sqrtf(v1), k[K_IBS], k[K_EPS]);
-  float w1 = fmaf(-k[K_SS], m1 / den, w0 * k[K_DEC]);
+  float w1 = fmaf(-k[K_SS], m1 / den, w0 * dec);
   *v1_out = v1;
   *w1_out = w1;
 }
 
-/* AdamW with every state in binary32 (no quantization). Used only to pin the
- * arithmetic above against torch.optim.AdamW. */
+/* AdamW (coupled = 0) or Adam (coupled = 1) with every state in binary32 (no
+ * quantization). Used only to pin the arithmetic above against
+ * torch.optim.AdamW / torch.optim.Adam. */
 void oracle_adamw_f32_tensor(int64_t n, const float* g, float* m, float* v, float* w,
-                             const oracle_hparams* hp, int64_t step) {
+                             const oracle_hparams* hp, int64_t step, int coupled) {
   float k[K_COUNT];
   oracle_adamw_constants(hp, step, k);
+  float dec = decay_factor(k, coupled);
   for (int64_t i = 0; i < n; ++i) {
-    float m1 = adamw_first_moment(k, g[i], m[i]);
+    float gd = effective_grad(k, coupled, g[i], w[i]);
+    float m1 = adamw_first_moment(k, gd, m[i]);
     float v1, w1;
-    adamw_second_moment_and_weight(k, g[i], m1, v[i], w[i], &v1, &w1);
+    adamw_second_moment_and_weight(k, dec, gd, m1, v[i], w[i], &v1, &w1);
     m[i] = m1;
     v[i] = v1;
     w[i] = w1;
@@ -360,11 +378,13 @@ void oracle_adamw_f32_tensor(int64_t n, const float* g, float* m, float* v, floa
  * Returns 0, or -1 on a bad format or allocation failure. */
 static int adamw_lowbit_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_scale_inv,
                                uint8_t* qm, float* m_meta, uint16_t* v, uint16_t* w,
-                               const oracle_hparams* hp, int64_t step, float* amax_w_out) {
+                               const oracle_hparams* hp, int64_t step, int coupled,
+                               float* amax_w_out) {
   const mf_format* gf = fp8_format(gfmt);
   if (!gf) return -1;
   float k[K_COUNT];
   oracle_adamw_constants(hp, step, k);
+  float dec = decay_factor(k, coupled);
   float m_scale_inv_old = m_meta[2];
 
   float* g = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
@@ -376,10 +396,11 @@ static int adamw_lowbit_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_s
   }
 
   /* Pass 1: dequantize gradient and old first moment, new first moment, and
-   * the amax of the new first moment (R-TWOPASS). */
+   * the amax of the new first moment (R-TWOPASS). g[] holds the gradient the
+   * moments see (R-ADAM). */
   uint32_t amax_m_bits = 0u;
   for (int64_t i = 0; i < n; ++i) {
-    g[i] = fp8_dec(gf, qg[i]) * g_scale_inv;
+    g[i] = effective_grad(k, coupled, fp8_dec(gf, qg[i]) * g_scale_inv, f16_dec(w[i]));
     float m0 = fp8_dec(&FMT_E4M3, qm[i]) * m_scale_inv_old;
     m1[i] = adamw_first_moment(k, g[i], m0);
     uint32_t u = f32_bits(m1[i]) & 0x7FFFFFFFu;
@@ -393,7 +414,7 @@ static int adamw_lowbit_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_s
   uint32_t amax_w_bits = 0u;
   for (int64_t i = 0; i < n; ++i) {
     float v1, w1;
-    adamw_second_moment_and_weight(k, g[i], m1[i], f16_dec(v[i]), f16_dec(w[i]), &v1, &w1);
+    adamw_second_moment_and_weight(k, dec, g[i], m1[i], f16_dec(v[i]), f16_dec(w[i]), &v1, &w1);
     v[i] = f16_enc(v1);
     w[i] = f16_enc(w1);
     qm[i] = fp8_enc(&FMT_E4M3, m1[i] * s_m);
@@ -410,22 +431,26 @@ static int adamw_lowbit_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_s
   return 0;
 }
 
-/* O2 step on one tensor (see adamw_lowbit_tensor for the arguments). */
+/* O2 step on one tensor (see adamw_lowbit_tensor for the arguments);
+ * coupled = 1 selects Adam (R-ADAM). */
 int oracle_adamw_o2_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_scale_inv,
                            uint8_t* qm, float* m_meta, uint16_t* v, uint16_t* w,
-                           const oracle_hparams* hp, int64_t step) {
-  return adamw_lowbit_tensor(n, qg, gfmt, g_scale_inv, qm, m_meta, v, w, hp, step, NULL);
+                           const oracle_hparams* hp, int64_t step, int coupled) {
+  return adamw_lowbit_tensor(n, qg, gfmt, g_scale_inv, qm, m_meta, v, w, hp, step, coupled, NULL);
 }
 
-/* O3 step on one tensor: the O2 update applied to the FP16 master weight,
+/* O3 step on one tensor (coupled = 1: Adam): the O2 update applied to the
+ * FP16 master weight,
  * then the FP8 E4M3 regular-weight copy from the stored master (R-O3COPY):
  * amax_w over the new master, s_w = scale(amax_w, 448), w8[i] =
  * enc(master[i]*s_w); w8_meta receives {amax_w, s_w, 1/s_w}. */
 int oracle_adamw_o3_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_scale_inv,
                            uint8_t* qm, float* m_meta, uint16_t* v, uint16_t* master,
-                           uint8_t* w8, float* w8_meta, const oracle_hparams* hp, int64_t step) {
+                           uint8_t* w8, float* w8_meta, const oracle_hparams* hp, int64_t step,
+                           int coupled) {
   float amax_w = 0.0f;
-  int rc = adamw_lowbit_tensor(n, qg, gfmt, g_scale_inv, qm, m_meta, v, master, hp, step, &amax_w);
+  int rc = adamw_lowbit_tensor(n, qg, gfmt, g_scale_inv, qm, m_meta, v, master, hp, step, coupled,
+                               &amax_w);
   if (rc != 0) return rc;
   float s_w = oracle_scale(amax_w, (float)mf_max(&FMT_E4M3));
   for (int64_t i = 0; i < n; ++i) w8[i] = fp8_enc(&FMT_E4M3, f16_dec(master[i]) * s_w);

@@ -34,7 +34,8 @@ def exact_constants(step, lr, betas, eps, weight_decay):
     b1, b2 = betas
     bc1 = 1.0 - b1 ** step
     bc2 = 1.0 - b2 ** step
-    vals = [b1, 1.0 - b1, b2, 1.0 - b2, eps, lr / bc1, 1.0 / bc2 ** 0.5, 1.0 - lr * weight_decay]
+    vals = [b1, 1.0 - b1, b2, 1.0 - b2, eps, lr / bc1, 1.0 / bc2 ** 0.5, 1.0 - lr * weight_decay,
+            weight_decay]
     return [F.of(v) for v in vals]
 
 
@@ -48,10 +49,13 @@ def exact_scale(amax: F, fmax: float) -> F:
     return s
 
 
-def exact_step(state, g32, gfmt, step, hp=HP, level="O2"):
+def exact_step(state, g32, gfmt, step, hp=HP, level="O2", adam=False):
     """One step on python lists of bit patterns. state: dict with w (fp16
-    bits), v (fp16 bits), m (E4M3 codes), m_si (F), and for O3 w8, w8_meta."""
-    B1, OB1, B2, OB2, EPS, SS, IBS, DEC = exact_constants(step, **hp)
+    bits), v (fp16 bits), m (E4M3 codes), m_si (F), and for O3 w8, w8_meta.
+    adam=True: torch.optim.Adam's coupled L2 (g + wd*w, no decoupled decay)."""
+    B1, OB1, B2, OB2, EPS, SS, IBS, DEC, WD = exact_constants(step, **hp)
+    if adam:
+        DEC = F.of(1.0)
     fmax_g = O.fp8_max(gfmt)
     # gradient quantization
     amax_g = max(float_to_bits(float(x)) & 0x7FFFFFFF for x in g32) if len(g32) else 0
@@ -65,6 +69,8 @@ def exact_step(state, g32, gfmt, step, hp=HP, level="O2"):
     gs, m1s = [], []
     for i in range(len(g32)):
         g = fp8_value(qg[i], gfmt) * si_g
+        if adam:
+            g = F.fma(WD, f16_value(state["w"][i]), g)
         m0 = fp8_value(state["m"][i], 0) * state["m_si"]
         m1 = F.fma(B1, m0, OB1 * g)
         gs.append(g)
@@ -105,15 +111,15 @@ def u32(a):
     return [int(x) for x in np.asarray(a, np.float32).view(np.uint32)[:3]]
 
 
-def run_both(w_bits, grads, gfmt, level, hp=HP):
+def run_both(w_bits, grads, gfmt, level, hp=HP, adam=False):
     """Run the oracle and the exact reference side by side; assert bitwise
     agreement after every step. Returns the oracle state."""
-    ost = O.TensorState(np.array(w_bits, np.uint16), level)
+    ost = O.TensorState(np.array(w_bits, np.uint16), level, adam=adam)
     est = new_exact_state(w_bits)
     for t, g in enumerate(grads, start=1):
         g = np.asarray(g, np.float32)
         (qg, gmeta), = O.step_list([ost], [g], gfmt, t, **hp)
-        eqg, egmeta = exact_step(est, g, gfmt, t, hp, level)
+        eqg, egmeta = exact_step(est, g, gfmt, t, hp, level, adam)
         assert list(qg) == eqg, ("grad codes", t)
         assert u32(gmeta) == list(egmeta), ("grad meta", t)
         assert list(ost.m) == est["m"], ("m codes", t)
@@ -133,9 +139,10 @@ def run_both(w_bits, grads, gfmt, level, hp=HP):
 def test_constants_hand_computed():
     k1 = O.adamw_constants(1, **HP).view(np.uint32)
     k2 = O.adamw_constants(2, **HP).view(np.uint32)
-    # B1 OB1 B2 OB2 EPS SS IBS DEC
+    # B1 OB1 B2 OB2 EPS SS IBS DEC WD
     assert [hex(x) for x in k1] == ["0x3f666666", "0x3dcccccd", "0x3f7fbe77", "0x3a83126f",
-                                    "0x322bcc77", "0x3c23d70a", "0x41fcfb72", "0x3f7fff58"]
+                                    "0x322bcc77", "0x3c23d70a", "0x41fcfb72", "0x3f7fff58",
+                                    "0x3c23d70a"]
     assert hex(k2[5]) == "0x3bac7692" and hex(k2[6]) == "0x41b2ee20"
     assert [e.b for e in exact_constants(1, **HP)] == [int(x) for x in k1]
 
@@ -190,16 +197,31 @@ def test_worked_example_zero_gradient():
     assert list(st.m_meta[:3]) == [0.0, 1.0, 1.0]
 
 
+@pytest.mark.parametrize("adam", [False, True])
 @pytest.mark.parametrize("level", ["O2", "O3"])
 @pytest.mark.parametrize("gfmt", [O.E4M3, O.E5M2])
-def test_random_tiny_tensors_match_exact_arithmetic(level, gfmt):
-    rng = np.random.default_rng(17 + gfmt + (level == "O3") * 2)
+def test_random_tiny_tensors_match_exact_arithmetic(level, gfmt, adam):
+    rng = np.random.default_rng(17 + gfmt + (level == "O3") * 2 + adam * 4)
     n = 6
     w = O.f16_encode((rng.standard_normal(n) * 0.5).astype(np.float32))
     hp = dict(lr=3e-2, betas=(0.8, 0.95), eps=1e-6, weight_decay=0.1)
     grads = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 1, n)).astype(np.float32) for _ in range(3)]
     grads[1][2] = 0.0
-    run_both(list(w), grads, gfmt, level, hp)
+    run_both(list(w), grads, gfmt, level, hp, adam)
+
+
+def test_adam_differs_from_adamw_only_through_weight_decay():
+    """With wd = 0 Adam and AdamW are the same algorithm; with wd > 0 the
+    coupled L2 term changes the moments (and so the stored codes)."""
+    rng = np.random.default_rng(5)
+    w = O.f16_encode((rng.standard_normal(512) * 0.1).astype(np.float32))
+    g = (rng.standard_normal(512) * 1e-3).astype(np.float32)
+    for wd, same in ((0.0, True), (0.1, False)):
+        a = O.TensorState(w, "O2", adam=True)
+        b = O.TensorState(w, "O2", adam=False)
+        O.step_list([a], [g], O.E4M3, 1, lr=1e-3, weight_decay=wd)
+        O.step_list([b], [g], O.E4M3, 1, lr=1e-3, weight_decay=wd)
+        assert np.array_equal(a.w, b.w) == same and np.array_equal(a.m, b.m) == same
 
 
 # ---------------------------------------------------------------------------
@@ -233,6 +255,39 @@ def test_fp32_storage_matches_torch_adamw():
         # weights that cross zero carry the rounding of lr-sized updates:
         # absolute tolerance one millionth of lr
         np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-5, atol=1e-6 * lr)
+
+
+def test_adam_fp32_storage_matches_torch_adam():
+    """Coupled L2 variant against torch.optim.Adam (weight_decay adds wd*w to
+    the gradient before the moments)."""
+    rng = np.random.default_rng(1)
+    n = 4096
+    lr, betas, eps, wd = 2e-2, (0.8, 0.95), 1e-6, 0.1
+    w0 = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.Adam([p], lr=lr, betas=betas, eps=eps, weight_decay=wd, foreach=False)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w = w0.copy()
+    mag = np.zeros(n)
+    for t in range(1, 11):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-9, 0, n)).astype(np.float32)
+        mag = betas[0] * mag + (1 - betas[0]) * (np.abs(g) + wd * np.abs(w))
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        O.adamw_f32_tensor(g, m, v, w, t, adam=True, lr=lr, betas=betas, eps=eps, weight_decay=wd)
+        st = opt.state[p]
+        assert (np.abs(m - st["exp_avg"].numpy()) <= 1e-5 * mag).all()
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-5, atol=1e-30)
+        np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-5, atol=1e-6 * lr)
+    # and it is not AdamW: decoupled decay gives a different trajectory
+    w2, m2, v2 = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rng = np.random.default_rng(1)
+    rng.standard_normal(n)
+    for t in range(1, 11):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-9, 0, n)).astype(np.float32)
+        O.adamw_f32_tensor(g, m2, v2, w2, t, adam=False, lr=lr, betas=betas, eps=eps, weight_decay=wd)
+    assert np.abs(w2 - w).max() > 1e-3
 
 
 def test_quantized_trajectory_tracks_fp32_trajectory():
