@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama2_7b",
                    help="llama2_7b (default), llama2_13b, gpt2_small, single_1m, stress")
+    p.add_argument("--optimizer", default="adamw", choices=("adamw", "adam"),
+                   help="adamw (decoupled decay, default) or adam (coupled L2)")
     p.add_argument("--shard", type=int, default=1,
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -88,13 +90,14 @@ def calibrate_copy(gib: float) -> None:
 class State:
     """Device state of a workload plus two resident binary32 gradient sets."""
 
-    def __init__(self, w, device):
+    def __init__(self, w, device, adam: bool = False):
         import torch
 
         import bit_adamw_optimizer_amd as M
         from bit_adamw_optimizer_amd import workloads as W
 
         self.w = w
+        self.adam = adam
         # every role lives in one allocation (views per tensor)
         self.weights = W.init_weights(w, device, out=M.flat_views(w.numel, torch.float16, device))
         st = M.allocate_state(self.weights, w.level, flat=True)
@@ -122,12 +125,13 @@ class State:
         M.amax(g32, self.grad_meta)
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2":
-            M.adamw_o2_step(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
-                            self.tl_v, self.tl_w, step=step, **w.hparams())
+            fn = M.adam_o2_step if self.adam else M.adamw_o2_step
+            fn(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+               self.tl_v, self.tl_w, step=step, **w.hparams())
         else:
-            M.adamw_o3_step(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
-                            self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step,
-                            **w.hparams())
+            fn = M.adam_o3_step if self.adam else M.adamw_o3_step
+            fn(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+               self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step, **w.hparams())
 
 
 def cpu_baseline(w, device, threads: int) -> dict:
@@ -326,7 +330,8 @@ def main() -> int:
     w = W.make(args.workload, shard=args.shard)
     print("bench: %s, %s, %d tensors, %d params; setting up" % (w.name, w.level, w.n, w.params),
           file=sys.stderr, flush=True)
-    st = State(w, device)
+    adam = args.optimizer == "adam"
+    st = State(w, device, adam=adam)
 
     step = 0
     for _ in range(args.warmup):
@@ -353,12 +358,14 @@ def main() -> int:
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     P = w.params
-    step_bytes = PASS1_BYTES + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+    # Adam's pass 1 also reads the FP16 weight for its L2 term
+    pass1_bytes = PASS1_BYTES + (2 if adam else 0)
+    step_bytes = pass1_bytes + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
     path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
     gbps = path_bytes * P / (ms_per_step * 1e-3) / 1e9
 
     per_kernel_bytes = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES,
-                        "step_pass1": PASS1_BYTES, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
+                        "step_pass1": pass1_bytes, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
                         "o3_pass3": PASS3_BYTES}
     breakdown = {}
     for k, d in kernels.items():
@@ -389,10 +396,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: %s FP8 AdamW step, %d tensors, %d params, %s grads "
+        "config": {"workload": "%s: %s FP8 %s step, %d tensors, %d params, %s grads "
                                "(amax + quantize + step per iteration)"
-                               % (w.name, w.level, w.n, P, "E4M3" if w.grad_fmt == 0 else "E5M2"),
-                   "level": w.level, "tensors": w.n, "params": P},
+                               % (w.name, w.level, "Adam" if adam else "AdamW", w.n, P,
+                                  "E4M3" if w.grad_fmt == 0 else "E5M2"),
+                   "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P},
         "hbm_gbps": round(gbps, 1),
         "pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_param": path_bytes,

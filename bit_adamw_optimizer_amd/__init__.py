@@ -29,7 +29,8 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "MsampError", "TensorList", "lib", "amax", "quantize_fp8",
-    "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "codec_probe", "new_meta",
+    "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
+    "codec_probe", "new_meta",
     "allocate_state", "flat_views", "state_bytes_per_param", "profile_enable", "profile_read",
     "KERNELS", "release_cache", "library_path",
 ]
@@ -101,6 +102,10 @@ def lib():
         L.msamp_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(_HParams), i64, vp]
         L.msamp_adamw_o3_step.restype = st
+        L.msamp_adam_o2_step.argtypes = L.msamp_adamw_o2_step.argtypes
+        L.msamp_adam_o2_step.restype = st
+        L.msamp_adam_o3_step.argtypes = L.msamp_adamw_o3_step.argtypes
+        L.msamp_adam_o3_step.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -245,7 +250,8 @@ def dequantize_fp8(q, fmt: int, meta: torch.Tensor, out) -> None:
 
 
 def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
-                  *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int) -> None:
+                  *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int,
+                  _entry: str = "msamp_adamw_o2_step") -> None:
     """One in-place AdamW step in the O2 layout (see include/msamp.h)."""
     g = _tl(grad, "u8", "grad")
     m = _tl(exp_avg, "u8", "exp_avg")
@@ -256,7 +262,7 @@ def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
     if g.n == 0:
         return
     hp = _hp(lr, betas, eps, weight_decay)
-    _check(lib().msamp_adamw_o2_step(
+    _check(getattr(lib(), _entry)(
         g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
         m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
         ctypes.byref(hp), int(step), _stream(g.device)))
@@ -264,7 +270,7 @@ def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
 
 def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, master,
                   weight_fp8, weight_fp8_meta, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
-                  weight_decay=0.01, step: int) -> None:
+                  weight_decay=0.01, step: int, _entry: str = "msamp_adamw_o3_step") -> None:
     """One in-place AdamW step in the O3 layout (see include/msamp.h)."""
     g = _tl(grad, "u8", "grad")
     m = _tl(exp_avg, "u8", "exp_avg")
@@ -276,11 +282,23 @@ def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
     if g.n == 0:
         return
     hp = _hp(lr, betas, eps, weight_decay)
-    _check(lib().msamp_adamw_o3_step(
+    _check(getattr(lib(), _entry)(
         g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
         m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
         w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
         ctypes.byref(hp), int(step), _stream(g.device)))
+
+
+def adam_o2_step(*args, **kw) -> None:
+    """One in-place Adam (coupled L2) step in the O2 layout; arguments as
+    adamw_o2_step (see msamp_adam_o2_step in include/msamp.h)."""
+    adamw_o2_step(*args, _entry="msamp_adam_o2_step", **kw)
+
+
+def adam_o3_step(*args, **kw) -> None:
+    """One in-place Adam (coupled L2) step in the O3 layout; arguments as
+    adamw_o3_step (see msamp_adam_o3_step in include/msamp.h)."""
+    adamw_o3_step(*args, _entry="msamp_adam_o3_step", **kw)
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:

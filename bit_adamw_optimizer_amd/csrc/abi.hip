@@ -342,8 +342,9 @@ msamp_status check_hparams(const msamp_adamw_hparams* hp, int64_t step) {
   return MSAMP_OK;
 }
 
-// AdamW constants: binary64 expressions, each rounded once to binary32.
-StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step) {
+// AdamW / Adam constants: binary64 expressions, each rounded once to
+// binary32. Adam (coupled L2) has no decoupled decay: dec is exactly 1.
+StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled) {
   const double t = (double)step;
   const double bc1 = 1.0 - std::pow(hp->beta1, t);
   const double bc2 = 1.0 - std::pow(hp->beta2, t);
@@ -355,7 +356,8 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step) {
   k.eps = (float)hp->eps;
   k.ss = (float)(hp->lr / bc1);
   k.ibs = (float)(1.0 / std::sqrt(bc2));
-  k.dec = (float)(1.0 - hp->lr * hp->weight_decay);
+  k.dec = coupled ? 1.0f : (float)(1.0 - hp->lr * hp->weight_decay);
+  k.wd = (float)hp->weight_decay;
   return k;
 }
 
@@ -371,7 +373,7 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step) {
     if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
   } while (0)
 
-msamp_status step_impl(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
+msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, const uint8_t* const* grad,
                        int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
                        msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
                        uint16_t* const* weight, uint8_t* const* weight_fp8,
@@ -398,13 +400,13 @@ msamp_status step_impl(bool o3, int32_t n, const int64_t* numel, const uint8_t* 
                                  (const void* const*)weight_fp8};
   Plan* p = nullptr;
   MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p));
-  const StepConsts k = make_consts(hp, step);
+  const StepConsts k = make_consts(hp, step, coupled);
 
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
-               launch_step_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
+               launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, k, s));
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
-               launch_step_pass2(grad_fmt, o3, p->desc, p->chunks, p->nchunks, grad_meta,
+               launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
@@ -520,7 +522,18 @@ msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t*
                                  uint16_t* const* exp_avg_sq, uint16_t* const* weight,
                                  const msamp_adamw_hparams* hp, int64_t step, void* stream) {
   return guarded([&]() {
-    return step_impl(false, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+    return step_impl(false, false, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                     exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adam_o2_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_impl(false, true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                      exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
   });
 }
@@ -532,7 +545,19 @@ msamp_status msamp_adamw_o3_step(int32_t n, const int64_t* numel, const uint8_t*
                                  uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                  const msamp_adamw_hparams* hp, int64_t step, void* stream) {
   return guarded([&]() {
-    return step_impl(true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+    return step_impl(true, false, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                     exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adam_o3_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_impl(true, true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                      exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, stream);
   });
 }

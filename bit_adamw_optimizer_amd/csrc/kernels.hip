@@ -270,6 +270,13 @@ __device__ __forceinline__ float first_moment(const StepConsts& k, float g, floa
   return __builtin_fmaf(k.b1, m0, k.ob1 * g);
 }
 
+// The gradient the moments see: g for AdamW; g + wd*w0 (one fused
+// multiply-add) for Adam's coupled L2 term.
+template <bool COUPLED>
+__device__ __forceinline__ float effective_grad(const StepConsts& k, float g, float w0) {
+  return COUPLED ? __builtin_fmaf(k.wd, w0, g) : g;
+}
+
 // v1, den and w1 (see the AdamW definition in msamp.h).
 __device__ __forceinline__ void second_moment_and_weight(const StepConsts& k, float g, float m1,
                                                          float v0, float w0, float& v1,
@@ -279,8 +286,9 @@ __device__ __forceinline__ void second_moment_and_weight(const StepConsts& k, fl
   w1 = __builtin_fmaf(-k.ss, m1 / den, w0 * k.dec);
 }
 
-// Pass 1 (O2 and O3): new first moment and its per-tensor amax.
-template <int GF>
+// Pass 1 (O2 and O3): new first moment and its per-tensor amax. Adam
+// (COUPLED) also reads the weight for its L2 term.
+template <int GF, bool COUPLED>
 __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
@@ -292,24 +300,34 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   const float msi = mmeta[r.t].scale_inv;
   const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
   const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   uint32_t mx = 0u;
   for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
     if (e1 + 8 <= r.end) {
       const u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
       const u32x2 M0 = load<u32x2>(mq + e0), M1 = load<u32x2>(mq + e1);
-      float g[16], m[16];
+      float g[16], m[16], w[16];
+      if (COUPLED) {
+        h8_to_f8(load<u32x4>(wh + e0), w);
+        h8_to_f8(load<u32x4>(wh + e1), w + 8);
+      }
       dec8<GF>(G0, g);
       dec8<GF>(G1, g + 8);
       dec8<kE4M3>(M0, m);
       dec8<kE4M3>(M1, m + 8);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = umax(mx, abs_bits(first_moment(k, g[e] * gsi, m[e] * msi)));
+      for (int e = 0; e < 16; ++e) {
+        const float ge = effective_grad<COUPLED>(k, g[e] * gsi, COUPLED ? w[e] : 0.0f);
+        mx = umax(mx, abs_bits(first_moment(k, ge, m[e] * msi)));
+      }
     } else {
       for (int h = 0; h < 2; ++h) {
         const int64_t e = h ? e1 : e0;
-        for (int64_t i = e; i < e + 8 && i < r.end; ++i)
-          mx = umax(mx, abs_bits(first_moment(k, dec1<GF>(gq[i]) * gsi, dec1<kE4M3>(mq[i]) * msi)));
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          const float ge = effective_grad<COUPLED>(k, dec1<GF>(gq[i]) * gsi, COUPLED ? h_to_f(wh[i]) : 0.0f);
+          mx = umax(mx, abs_bits(first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi)));
+        }
       }
     }
   }
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
 // Pass 2: recompute m1 exactly as in pass 1, then v1, w1; store m (E4M3 with
 // the new scale), v and w (FP16). In the O3 layout the weight is the master
 // and the amax of the stored master is reduced into amax_w.
-template <int GF, bool O3>
+template <int GF, bool O3, bool COUPLED>
 __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
       h8_to_f8(W1, w + 8);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float ge = g[e] * gsi;
+        const float ge = effective_grad<COUPLED>(k, g[e] * gsi, w[e]);
         const float m1 = first_moment(k, ge, m[e] * msi);
         float v1, w1;
         second_moment_and_weight(k, ge, m1, v[e], w[e], v1, w1);
@@ -379,10 +397,11 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
       for (int h = 0; h < 2; ++h) {
         const int64_t e = h ? e1 : e0;
         for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
-          const float ge = dec1<GF>(gq[i]) * gsi;
+          const float w0 = h_to_f(wh[i]);
+          const float ge = effective_grad<COUPLED>(k, dec1<GF>(gq[i]) * gsi, w0);
           const float m1 = first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi);
           float v1, w1;
-          second_moment_and_weight(k, ge, m1, h_to_f(vh[i]), h_to_f(wh[i]), v1, w1);
+          second_moment_and_weight(k, ge, m1, h_to_f(vh[i]), w0, v1, w1);
           float mm[4] = {m1 * s_m, 0.0f, 0.0f, 0.0f};
           mq[i] = (uint8_t)(enc4<kE4M3>(mm) & 0xFFu);
           vh[i] = f_to_h(v1);
@@ -538,34 +557,59 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
   return hipGetLastError();
 }
 
-hipError_t launch_step_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+template <int GF, bool COUPLED>
+static void pass1_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
+                         const msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                         const StepConsts& k) {
+  k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+}
+
+hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream) {
   if (nchunks <= 0) return hipSuccess;
-  if (gfmt == kE4M3)
-    k_step_pass1<kE4M3><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
-  else
-    k_step_pass1<kE5M2><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+  const unsigned g = grid_of(nchunks);
+  if (gfmt == kE4M3) {
+    if (coupled) pass1_launch<kE4M3, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+    else pass1_launch<kE4M3, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+  } else {
+    if (coupled) pass1_launch<kE5M2, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+    else pass1_launch<kE5M2, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_step_pass2(int gfmt, bool o3, const TensorDesc* desc, const ChunkRef* chunks,
-                             int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
-                             const uint32_t* amax_m, uint32_t* amax_w, const StepConsts& k,
-                             hipStream_t stream) {
+template <int GF, bool O3, bool COUPLED>
+static void pass2_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
+                         const msamp_meta* gmeta, const msamp_meta* mmeta, const uint32_t* amax_m,
+                         uint32_t* amax_w, const StepConsts& k) {
+  k_step_pass2<GF, O3, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+}
+
+template <int GF>
+static void pass2_dispatch(bool o3, bool coupled, unsigned g, hipStream_t stream,
+                           const TensorDesc* desc, const ChunkRef* chunks, const msamp_meta* gmeta,
+                           const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
+                           const StepConsts& k) {
+  if (o3) {
+    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+  } else {
+    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+  }
+}
+
+hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
+                             const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
+                             const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
+                             const StepConsts& k, hipStream_t stream) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
-  if (gfmt == kE4M3) {
-    if (o3)
-      k_step_pass2<kE4M3, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-    else
-      k_step_pass2<kE4M3, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-  } else {
-    if (o3)
-      k_step_pass2<kE5M2, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-    else
-      k_step_pass2<kE5M2, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-  }
+  if (gfmt == kE4M3)
+    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+  else
+    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
   return hipGetLastError();
 }
 

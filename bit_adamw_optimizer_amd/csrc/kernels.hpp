@@ -41,9 +41,11 @@ struct ChunkRef {
   int32_t chunk;
 };
 
-// AdamW constants of one step (binary64 expressions rounded once).
+// AdamW / Adam constants of one step (binary64 expressions rounded once).
+// dec is 1 - lr*wd for AdamW and exactly 1 for Adam; wd is the coupled L2
+// coefficient used by Adam only.
 struct StepConsts {
-  float b1, ob1, b2, ob2, eps, ss, ibs, dec;
+  float b1, ob1, b2, ob2, eps, ss, ibs, dec, wd;
 };
 
 // Every launcher enqueues one kernel on 'stream' and returns the launch
@@ -56,13 +58,15 @@ hipError_t launch_quantize(int fmt, const TensorDesc* desc, const ChunkRef* chun
                            int64_t nchunks, msamp_meta* meta, hipStream_t stream);
 hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* meta, hipStream_t stream);
-hipError_t launch_step_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+// 'coupled' selects Adam (L2 term wd*w added to the gradient before the
+// moments); otherwise AdamW.
+hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream);
-hipError_t launch_step_pass2(int gfmt, bool o3, const TensorDesc* desc, const ChunkRef* chunks,
-                             int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
-                             const uint32_t* amax_m, uint32_t* amax_w, const StepConsts& k,
-                             hipStream_t stream);
+hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
+                             const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
+                             const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
+                             const StepConsts& k, hipStream_t stream);
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
                            const uint32_t* amax_w, hipStream_t stream);
 // meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then

@@ -192,6 +192,28 @@ msamp_status msamp_adamw_o3_step(int32_t n, const int64_t* numel, const uint8_t*
                                  uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                  const msamp_adamw_hparams* hp, int64_t step, void* stream);
 
+/*
+ * msamp_adam_o2_step / msamp_adam_o3_step -- the same steps for
+ * torch.optim.Adam, the other optimizer the MS-AMP README recognizes ([RD]
+ * "Usage"): weight decay is an L2 term added to the gradient before the
+ * moments, gd = fma(WD, w0, g) with WD = (float)weight_decay and w0 the
+ * weight (O2) or master (O3) before the step, and the update has no
+ * decoupled decay (DEC = 1). Arguments, layouts and errors as for the AdamW
+ * entry points. Pass 1 also reads the weight: 15 bytes per element (O2),
+ * 18 (O3).
+ */
+msamp_status msamp_adam_o2_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream);
+msamp_status msamp_adam_o3_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
 /* Frees every cached device table of the library (all devices) after
  * waiting for the devices to finish. Safe to call at any time from one
  * thread while no other library call runs. */

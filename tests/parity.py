@@ -79,9 +79,10 @@ def u32(a) -> np.ndarray:
 class GpuState:
     """Device state of one workload, driven through the C ABI."""
 
-    def __init__(self, w: W.Workload, device):
+    def __init__(self, w: W.Workload, device, adam: bool = False):
         self.w = w
         self.device = device
+        self.adam = adam  # Adam (coupled L2) instead of AdamW
         self.weights = W.init_weights(w, device)  # FP16 weight (O2) or master (O3)
         st = M.allocate_state(self.weights, w.level)
         self.exp_avg = st["exp_avg"]
@@ -109,12 +110,13 @@ class GpuState:
         M.amax(self.tl_g32, self.grad_meta)
         M.quantize_fp8(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq)
         if w.level == "O2":
-            M.adamw_o2_step(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
-                            self.tl_v, self.tl_w, step=step, **w.hparams())
+            fn = M.adam_o2_step if self.adam else M.adamw_o2_step
+            fn(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+               self.tl_v, self.tl_w, step=step, **w.hparams())
         else:
-            M.adamw_o3_step(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
-                            self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step,
-                            **w.hparams())
+            fn = M.adam_o3_step if self.adam else M.adamw_o3_step
+            fn(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
+               self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step, **w.hparams())
 
 
 def host(t: torch.Tensor) -> np.ndarray:
@@ -124,14 +126,16 @@ def host(t: torch.Tensor) -> np.ndarray:
     return x
 
 
-def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda"):
+def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda",
+               adam: bool = False):
     """Runs 'steps' steps on the GPU and on the oracle (for the tensors in
-    'verify', default all) and returns a dict of Stats per output."""
+    'verify', default all) and returns a dict of Stats per output. adam=True
+    runs the Adam (coupled L2) entry points instead of AdamW."""
     verify = list(range(w.n)) if verify is None else list(verify)
     t0 = time.time()
-    gs = GpuState(w, device)
+    gs = GpuState(w, device, adam=adam)
     torch.cuda.synchronize()
-    ost = {t: O.TensorState(host(gs.weights[t]), w.level) for t in verify}
+    ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam) for t in verify}
     stats = {k: Stats() for k in ("m", "v", "w", "w8", "m_meta", "w8_meta")}
     pool = ThreadPoolExecutor(max_workers=threads)
     hp = w.hparams()

@@ -57,6 +57,28 @@ def test_tiny_stress_e5m2_10_steps():
         assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
 
 
+@pytest.mark.parametrize("level", ["O2", "O3"])
+def test_adam_coupled_l2_10_steps(level):
+    """torch.optim.Adam variant (MS-AMP README, Usage): L2 weight decay on the
+    gradient, no decoupled decay."""
+    w = W.make("tiny_llama_o3" if level == "O3" else "tiny_llama")
+    w.weight_decay = 0.1
+    log("Adam %s tiny_llama, %d params" % (level, w.params))
+    stats, _, _ = run_parity(w, 10, adam=True)
+    _report("adam_" + level, stats)
+    assert_bar(stats)
+
+
+def test_adam_ragged_e5m2():
+    sizes = [0, 1, 15, 17, 4097, 65537, 131072 + 4096 + 9]
+    w = W.Workload("adam_ragged", "O2", W.E5M2, 4, ["t%d" % i for i in range(len(sizes))], sizes,
+                   grad_kind="student_t3", lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.2,
+                   seed_base=14)
+    stats, _, _ = run_parity(w, 4, adam=True)
+    _report(w.name, stats)
+    assert_bar(stats)
+
+
 def test_ragged_sizes_o2_and_o3():
     """Sizes around the 16-element vector, the 4096-element tile and the
     65536-element chunk, including empty tensors."""
