@@ -87,3 +87,44 @@ def test_f16_decode_all_patterns():
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     fin = ~np.isnan(ref)
     assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+
+
+@pytest.mark.parametrize("op,kind", [(M.PROBE_F32_TO_E4M3, O.E4M3), (M.PROBE_F32_TO_E5M2, O.E5M2),
+                                     (M.PROBE_F32_TO_F16, "f16")])
+def test_exhaustive_every_binary32_input(op, kind):
+    """All 2^32 binary32 bit patterns through the device cast, against the
+    oracle's encoder (bit-exact; FP16 NaN payloads are only checked to stay
+    NaN)."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 28
+    sub = chunk // 16
+    pool = ThreadPoolExecutor(max_workers=16)
+    out_dtype = torch.uint8 if kind != "f16" else torch.int16
+    bad_total = 0
+    for start in range(0, 1 << 32, chunk):
+        log("exhaustive %s chunk %d/16" % (kind, start // chunk + 1))
+        host_bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        x = torch.from_numpy(host_bits.view(np.int32)).to(DEV)
+        out = torch.empty(chunk, dtype=out_dtype, device=DEV)
+        M.codec_probe(op, x, out)
+        got = out.cpu().numpy()
+        xf = host_bits.view(np.float32)
+        if kind == "f16":
+            ref = np.concatenate(list(pool.map(O.f16_encode, [xf[i:i + sub] for i in range(0, chunk, sub)])))
+            got = got.view(np.uint16)
+            nan = np.isnan(xf)
+            bad = (got != ref) & ~nan
+            assert np.isnan(got[nan].view(np.float16)).all()
+        else:
+            ref = np.concatenate(list(pool.map(lambda a: O.fp8_encode(a, kind),
+                                               [xf[i:i + sub] for i in range(0, chunk, sub)])))
+            bad = got != ref
+        nbad = int(bad.sum())
+        if nbad:
+            i = np.nonzero(bad)[0][:5]
+            raise AssertionError("%s: %d mismatches in chunk at %#x, e.g. %s" % (
+                kind, nbad, start, [(hex(int(host_bits[j])), int(got[j]), int(ref[j])) for j in i]))
+        bad_total += nbad
+        del x, out
+    pool.shutdown()
+    assert bad_total == 0
