@@ -157,6 +157,12 @@ __device__ __forceinline__ int64_t group8_base(int64_t tile) {
   return tile + (threadIdx.x >> 6) * 1024 + (threadIdx.x & 63) * 8;
 }
 
+// First element of this lane's 16-element group (FP8-only layout: one
+// 16-byte access per stream, 1 KB per wave instruction).
+__device__ __forceinline__ int64_t group16_base(int64_t tile) {
+  return tile + (threadIdx.x >> 6) * 1024 + (threadIdx.x & 63) * 16;
+}
+
 // First element of this lane's 4-element group k (FP32 layout).
 __device__ __forceinline__ int64_t group4_base(int64_t tile, int k) {
   return tile + (threadIdx.x >> 6) * 1024 + k * 256 + (threadIdx.x & 63) * 4;
@@ -304,23 +310,37 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   uint32_t mx = 0u;
   for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
-    if (e1 + 8 <= r.end) {
+    if (!COUPLED && group16_base(tile) + 16 <= r.end) {
+      // only FP8 streams: 16 consecutive codes per lane, one 16-byte
+      // non-temporal load per stream
+      const int64_t e = group16_base(tile);
+      const u32x4 G = load_stream<u32x4>(gq + e), Mq = load_stream<u32x4>(mq + e);
+      float g[16], m[16];
+      dec8<GF>(G.xy, g);
+      dec8<GF>(G.zw, g + 8);
+      dec8<kE4M3>(Mq.xy, m);
+      dec8<kE4M3>(Mq.zw, m + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = umax(mx, abs_bits(first_moment(k, g[i] * gsi, m[i] * msi)));
+    } else if (COUPLED && e1 + 8 <= r.end) {
       const u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
       const u32x2 M0 = load<u32x2>(mq + e0), M1 = load<u32x2>(mq + e1);
       float g[16], m[16], w[16];
-      if (COUPLED) {
-        h8_to_f8(load<u32x4>(wh + e0), w);
-        h8_to_f8(load<u32x4>(wh + e1), w + 8);
-      }
+      h8_to_f8(load<u32x4>(wh + e0), w);
+      h8_to_f8(load<u32x4>(wh + e1), w + 8);
       dec8<GF>(G0, g);
       dec8<GF>(G1, g + 8);
       dec8<kE4M3>(M0, m);
       dec8<kE4M3>(M1, m + 8);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float ge = effective_grad<COUPLED>(k, g[e] * gsi, COUPLED ? w[e] : 0.0f);
+        const float ge = effective_grad<COUPLED>(k, g[e] * gsi, w[e]);
         mx = umax(mx, abs_bits(first_moment(k, ge, m[e] * msi)));
       }
+    } else if (!COUPLED) {
+      const int64_t e = group16_base(tile);
+      for (int64_t i = e; i < e + 16 && i < r.end; ++i)
+        mx = umax(mx, abs_bits(first_moment(k, dec1<GF>(gq[i]) * gsi, dec1<kE4M3>(mq[i]) * msi)));
     } else {
       for (int h = 0; h < 2; ++h) {
         const int64_t e = h ? e1 : e0;
