@@ -134,6 +134,29 @@ class State:
                self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step, **w.hparams())
 
 
+def numerics_report(st) -> dict:
+    """Value statistics of the stored state after the timed steps: fractions
+    of the FP16 second moment that are +-0 or subnormal (binary16 underflows
+    (1-b2)*g^2 at small gradient scales) and of first-moment codes at 0 and
+    at +-max (0x7E)."""
+    import torch
+
+    n = zero = sub = 0
+    m_zero = m_max = 0
+    for v in st.tl_v.tensors:
+        b = v.view(torch.int16)
+        mag = b & 0x7FFF
+        n += b.numel()
+        zero += int((mag == 0).sum())
+        sub += int(((mag > 0) & (mag < 0x0400)).sum())
+    for m in st.tl_m.tensors:
+        mag = m & 0x7F
+        m_zero += int((mag == 0).sum())
+        m_max += int((mag == 0x7E).sum())
+    return {"v_zero_frac": zero / n, "v_subnormal_frac": sub / n,
+            "m_code_zero_frac": m_zero / n, "m_code_max_frac": m_max / n}
+
+
 def cpu_baseline(w, device, threads: int) -> dict:
     """The oracle on a bounded sample of the workload: the tensors of the
     first layer (one full step each: gradient amax + quantize + the O2/O3
@@ -412,6 +435,7 @@ def main() -> int:
         "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),
     }
+    result["numerics"] = {k: round(v, 6) for k, v in numerics_report(st).items()}
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, device, args.cpu_threads)

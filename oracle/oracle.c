@@ -439,6 +439,43 @@ int oracle_adamw_o2_tensor(int64_t n, const uint8_t* qg, int gfmt, float g_scale
   return adamw_lowbit_tensor(n, qg, gfmt, g_scale_inv, qm, m_meta, v, w, hp, step, coupled, NULL);
 }
 
+/* Ablation (not the reading the step follows, see R-TWOPASS): the O2 step in
+ * one pass with delayed scaling of the first moment. The new codes are
+ * encoded with the scale of the previous step's amax, s = scale(m_meta[0]),
+ * and m_meta becomes {amax(m1), s, 1/s}: the amax feeds the next step's
+ * scale and 1/s decodes the codes stored now. Everything else as the O2 step
+ * (coupled = 1: Adam). At step 1 the scale is 1, so |m1| below 2^-10 is
+ * stored as 0; values above 448/s saturate. */
+int oracle_adamw_o2_tensor_delayed(int64_t n, const uint8_t* qg, int gfmt, float g_scale_inv,
+                                   uint8_t* qm, float* m_meta, uint16_t* v, uint16_t* w,
+                                   const oracle_hparams* hp, int64_t step, int coupled) {
+  const mf_format* gf = fp8_format(gfmt);
+  if (!gf) return -1;
+  float k[K_COUNT];
+  oracle_adamw_constants(hp, step, k);
+  float dec = decay_factor(k, coupled);
+  float m_scale_inv_old = m_meta[2];
+  float s_m = oracle_scale(m_meta[0], (float)mf_max(&FMT_E4M3));
+  uint32_t amax_m_bits = 0u;
+  for (int64_t i = 0; i < n; ++i) {
+    float w0 = f16_dec(w[i]);
+    float g = effective_grad(k, coupled, fp8_dec(gf, qg[i]) * g_scale_inv, w0);
+    float m0 = fp8_dec(&FMT_E4M3, qm[i]) * m_scale_inv_old;
+    float m1 = adamw_first_moment(k, g, m0);
+    uint32_t u = f32_bits(m1) & 0x7FFFFFFFu;
+    if (u > amax_m_bits) amax_m_bits = u;
+    float v1, w1;
+    adamw_second_moment_and_weight(k, dec, g, m1, f16_dec(v[i]), w0, &v1, &w1);
+    v[i] = f16_enc(v1);
+    w[i] = f16_enc(w1);
+    qm[i] = fp8_enc(&FMT_E4M3, m1 * s_m);
+  }
+  m_meta[0] = f32_from_bits(amax_m_bits);
+  m_meta[1] = s_m;
+  m_meta[2] = 1.0f / s_m;
+  return 0;
+}
+
 /* O3 step on one tensor (coupled = 1: Adam): the O2 update applied to the
  * FP16 master weight,
  * then the FP8 E4M3 regular-weight copy from the stored master (R-O3COPY):

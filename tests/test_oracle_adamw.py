@@ -290,6 +290,55 @@ def test_adam_fp32_storage_matches_torch_adam():
     assert np.abs(w2 - w).max() > 1e-3
 
 
+def exact_step_delayed(state, g32, gfmt, step, hp=HP):
+    """Exact-rational reference of the one-pass delayed-scaling ablation."""
+    B1, OB1, B2, OB2, EPS, SS, IBS, DEC, WD = exact_constants(step, **hp)
+    amax_g = max(float_to_bits(float(x)) & 0x7FFFFFFF for x in g32)
+    s_g = exact_scale(F(amax_g), O.fp8_max(gfmt))
+    si_g = F.of(1.0) / s_g
+    s_m = exact_scale(state["m_amax"], 448.0)
+    amax = 0
+    for i, x in enumerate(g32):
+        xs = F.of(float(x)) * s_g
+        g = fp8_value(brute_encode_fp8(xs.q, gfmt, bool(xs.b >> 31)), gfmt) * si_g
+        m1 = F.fma(B1, fp8_value(state["m"][i], 0) * state["m_si"], OB1 * g)
+        amax = max(amax, m1.b & 0x7FFFFFFF)
+        v1 = F.fma(B2, f16_value(state["v"][i]), OB2 * (g * g))
+        den = F.fma(v1.sqrt(), IBS, EPS)
+        w1 = F.fma(-SS, m1 / den, f16_value(state["w"][i]) * DEC)
+        state["v"][i] = brute_encode_f16(v1.q, bool(v1.b >> 31))
+        state["w"][i] = brute_encode_f16(w1.q, bool(w1.b >> 31))
+        ms = m1 * s_m
+        state["m"][i] = brute_encode_fp8(ms.q, 0, bool(ms.b >> 31))
+    state["m_amax"] = F(amax)
+    state["m_si"] = F.of(1.0) / s_m
+    return (amax, s_m.b, state["m_si"].b)
+
+
+def test_delayed_scaling_ablation_matches_exact_arithmetic_and_zeroes_m_at_step_1():
+    """One-pass delayed scaling of the first moment (an ablation, not the
+    step's reading): step 1 encodes m1 ~ 1e-4 with scale 1, below half the
+    smallest E4M3 subnormal, so m is stored as all zeros; later steps use the
+    previous amax and saturate when the moment grows."""
+    rng = np.random.default_rng(12)
+    n = 5
+    w = list(O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32)))
+    ost = O.TensorState(np.array(w, np.uint16), "O2", delayed=True)
+    est = {"w": [int(x) for x in w], "v": [0] * n, "m": [0] * n, "m_si": F.of(1.0),
+           "m_amax": F(0)}
+    for t in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3 * (4.0 if t == 3 else 1.0)).astype(np.float32)
+        O.step_list([ost], [g], O.E4M3, t, **HP)
+        meta = exact_step_delayed(est, g, O.E4M3, t)
+        assert list(ost.m) == est["m"] and list(ost.v) == est["v"] and list(ost.w) == est["w"]
+        assert u32(ost.m_meta) == list(meta)
+        if t == 1:
+            assert ((ost.m & 0x7F) == 0).all()  # +-0 everywhere: the failure mode of delayed scaling
+            assert ost.m_meta[1] == 1.0
+    # the gradient jump at step 3 pushes |m1| past 448/s: saturated codes
+    assert ((ost.m & 0x7F) == 0x7E).sum() >= 1
+
+
 def test_quantized_trajectory_tracks_fp32_trajectory():
     """O2 storage error only: after 10 steps w stays within the accumulated
     FP8-m / FP16 rounding of the binary32 AdamW trajectory."""
