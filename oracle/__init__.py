@@ -81,6 +81,8 @@ def lib():
         L.oracle_scale.restype = f32
         L.oracle_quantize_fp8.argtypes = [vp, i64, i32, f32, vp, vp]
         L.oracle_quantize_fp8.restype = i32
+        L.oracle_quantize_fp8_prescaled.argtypes = [vp, i64, i32, f32, i32, vp, vp]
+        L.oracle_quantize_fp8_prescaled.restype = i32
         L.oracle_dequantize_fp8.argtypes = [vp, i64, i32, f32, vp]
         L.oracle_dequantize_fp8.restype = i32
         L.oracle_adamw_constants.argtypes = [hp, i64, vp]
@@ -163,6 +165,18 @@ def quantize_fp8(x, fmt: int, amax_value=None):
     if lib().oracle_quantize_fp8(_ptr(x), x.size, fmt, float(np.float32(amax_value)),
                                  _ptr(meta), _ptr(q)) != 0:
         raise ValueError("bad FP8 format %r" % fmt)
+    return q, meta
+
+
+def quantize_fp8_prescaled(x, fmt: int, amax_value, world: int):
+    """O1 pre-scaled quantization with the common amax of 'world' ranks.
+    Returns (codes, meta float32[4] = {amax, scale, scale_inv, 0})."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.empty(x.shape, np.uint8)
+    meta = np.zeros(4, np.float32)
+    if lib().oracle_quantize_fp8_prescaled(_ptr(x), x.size, fmt, float(np.float32(amax_value)),
+                                           int(world), _ptr(meta), _ptr(q)) != 0:
+        raise ValueError("bad FP8 format or world size")
     return q, meta
 
 

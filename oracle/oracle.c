@@ -286,6 +286,26 @@ int oracle_quantize_fp8(const float* x, int64_t n, int fmt, float amax, float* m
   return 0;
 }
 
+/* Pre-scaled quantization for an FP8 gradient all-reduce over 'world' ranks
+ * (the O1 level of the MS-AMP optimization-level page: FP8 weight gradients
+ * and FP8 all-reduce). Reading: every rank uses the common amax of the
+ * gradient over all ranks (an all-reduce MAX the caller performs) and the
+ * scale s = scale(amax * world), with amax * world rounded to binary32, so
+ * that the sum of the 'world' ranks' values stays within the FP8 range.
+ * world = 1 is oracle_quantize_fp8. Returns -1 on a bad format or world < 1. */
+int oracle_quantize_fp8_prescaled(const float* x, int64_t n, int fmt, float amax, int world,
+                                  float* meta_out, uint8_t* q) {
+  const mf_format* f = fp8_format(fmt);
+  if (!f || world < 1) return -1;
+  float s = oracle_scale(amax * (float)world, (float)mf_max(f));
+  float s_inv = 1.0f / s;
+  for (int64_t i = 0; i < n; ++i) q[i] = fp8_enc(f, x[i] * s);
+  meta_out[0] = amax;
+  meta_out[1] = s;
+  meta_out[2] = s_inv;
+  return 0;
+}
+
 /* Dequantization: out[i] = dec(q[i]) * s_inv. */
 int oracle_dequantize_fp8(const uint8_t* q, int64_t n, int fmt, float s_inv, float* out) {
   const mf_format* f = fp8_format(fmt);

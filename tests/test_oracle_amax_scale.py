@@ -125,3 +125,32 @@ def test_dequantize_is_code_times_scale_inv():
     err = np.abs(d.astype(np.float64) - x)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * meta[2]) * 1.0000001
     assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_prescaled_quantize_for_fp8_allreduce(fmt):
+    """O1 (MS-AMP optimization-level table: FP8 weight gradient and FP8
+    all-reduce): with the common amax of N ranks and scale(amax * N), the
+    exact sum of the N ranks' scaled values never exceeds the FP8 range, and
+    world = 1 is the plain per-tensor quantize."""
+    rng = np.random.default_rng(21 + fmt)
+    fmax = O.fp8_max(fmt)
+    for world in (1, 2, 3, 8, 64):
+        ranks = [(rng.standard_t(3, 4096) * 1e-3 * rng.uniform(0.5, 2)).astype(np.float32)
+                 for _ in range(world)]
+        amax = max(O.amax(r) for r in ranks)  # what an all-reduce MAX returns
+        outs = [O.quantize_fp8_prescaled(r, fmt, amax, world) for r in ranks]
+        s = outs[0][1][1]
+        assert all(o[1][1] == s for o in outs)
+        assert s == O.scale(np.float32(amax) * np.float32(world), fmax)
+        # codes: the scaled value rounded on the FP8 grid (the plain encoder)
+        for r, (q, _) in zip(ranks, outs):
+            assert np.array_equal(q, O.fp8_encode(r * s, fmt))
+        # exact sum of the decoded (unscaled-back) codes stays within range
+        total = np.sum([O.fp8_decode(q, fmt).astype(np.float64) for q, _ in outs], axis=0)
+        assert np.abs(total).max() <= fmax * (1 + 2.0 ** -3)
+        if world == 1:
+            q1, m1 = O.quantize_fp8(ranks[0], fmt)
+            assert np.array_equal(q1, outs[0][0]) and np.array_equal(m1, outs[0][1])
+    with pytest.raises(ValueError):
+        O.quantize_fp8_prescaled(np.ones(3, np.float32), fmt, 1.0, 0)
