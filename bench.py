@@ -57,8 +57,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama2_7b",
                    help="llama2_7b (default), llama2_13b, gpt2_small, single_1m, stress")
-    p.add_argument("--optimizer", default="adamw", choices=("adamw", "adam"),
-                   help="adamw (decoupled decay, default) or adam (coupled L2)")
+    p.add_argument("--optimizer", default="adamw", choices=("adamw", "adam", "adamw-delayed"),
+                   help="adamw (decoupled decay, default), adam (coupled L2), or the one-pass "
+                        "delayed-scaling ablation adamw-delayed (O2 only)")
     p.add_argument("--shard", type=int, default=1,
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,7 +91,7 @@ def calibrate_copy(gib: float) -> None:
 class State:
     """Device state of a workload plus two resident binary32 gradient sets."""
 
-    def __init__(self, w, device, adam: bool = False):
+    def __init__(self, w, device, adam: bool = False, delayed: bool = False):
         import torch
 
         import bit_adamw_optimizer_amd as M
@@ -98,6 +99,7 @@ class State:
 
         self.w = w
         self.adam = adam
+        self.delayed = delayed
         # every role lives in one allocation (views per tensor)
         self.weights = W.init_weights(w, device, out=M.flat_views(w.numel, torch.float16, device))
         st = M.allocate_state(self.weights, w.level, flat=True)
@@ -126,6 +128,8 @@ class State:
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2":
             fn = M.adam_o2_step if self.adam else M.adamw_o2_step
+            if self.delayed:
+                fn = M.adamw_o2_step_delayed
             fn(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
                self.tl_v, self.tl_w, step=step, **w.hparams())
         else:
@@ -354,7 +358,11 @@ def main() -> int:
     print("bench: %s, %s, %d tensors, %d params; setting up" % (w.name, w.level, w.n, w.params),
           file=sys.stderr, flush=True)
     adam = args.optimizer == "adam"
-    st = State(w, device, adam=adam)
+    delayed = args.optimizer == "adamw-delayed"
+    if delayed and w.level != "O2":
+        print("the delayed-scaling ablation exists for the O2 layout only", file=sys.stderr)
+        return 2
+    st = State(w, device, adam=adam, delayed=delayed)
 
     step = 0
     for _ in range(args.warmup):
@@ -383,20 +391,20 @@ def main() -> int:
     P = w.params
     # Adam's pass 1 also reads the FP16 weight for its L2 term
     pass1_bytes = PASS1_BYTES + (2 if adam else 0)
-    step_bytes = pass1_bytes + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+    step_bytes = (0 if delayed else pass1_bytes) + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
     path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
     gbps = path_bytes * P / (ms_per_step * 1e-3) / 1e9
 
     per_kernel_bytes = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES,
                         "step_pass1": pass1_bytes, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
-                        "o3_pass3": PASS3_BYTES}
+                        "o3_pass3": PASS3_BYTES, "o2_delayed": PASS2_BYTES}
     breakdown = {}
     for k, d in kernels.items():
         e = {"avg_ms": round(d["avg_ms"], 4), "launches": d["launches"]}
         if k in per_kernel_bytes:
             e["GB/s"] = round(per_kernel_bytes[k] * P / (d["avg_ms"] * 1e-3) / 1e9, 1)
         breakdown[k] = e
-    dom = "o2_pass2" if w.level == "O2" else "o3_pass2"
+    dom = ("o2_delayed" if delayed else "o2_pass2") if w.level == "O2" else "o3_pass2"
     roofline = None
     if dom in kernels:
         achieved = per_kernel_bytes[dom] * P / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
@@ -421,7 +429,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "%s: %s FP8 %s step, %d tensors, %d params, %s grads "
                                "(amax + quantize + step per iteration)"
-                               % (w.name, w.level, "Adam" if adam else "AdamW", w.n, P,
+                               % (w.name, w.level, {"adam": "Adam", "adamw": "AdamW",
+                                                    "adamw-delayed": "AdamW one-pass delayed-scaling "
+                                                                     "ablation"}[args.optimizer],
+                                  w.n, P,
                                   "E4M3" if w.grad_fmt == 0 else "E5M2"),
                    "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P},
         "hbm_gbps": round(gbps, 1),

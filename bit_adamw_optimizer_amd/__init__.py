@@ -29,6 +29,7 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "MsampError", "TensorList", "lib", "amax", "quantize_fp8",
+    "quantize_fp8_prescaled",
     "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
     "codec_probe", "new_meta",
     "allocate_state", "flat_views", "state_bytes_per_param", "profile_enable", "profile_read",
@@ -47,7 +48,7 @@ PROBE_F16_TO_F32 = 5
 
 # kernel kinds of msamp_profile_read, in enum order
 KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
-           "o3_pass3", "finalize", "amax_finalize"]
+           "o3_pass3", "finalize", "amax_finalize", "o2_delayed"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
@@ -94,6 +95,8 @@ def lib():
         L.msamp_amax.restype = st
         L.msamp_quantize_fp8.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp]
         L.msamp_quantize_fp8.restype = st
+        L.msamp_quantize_fp8_prescaled.argtypes = [i32, vp, vp, ctypes.c_int, vp, i32, vp, vp]
+        L.msamp_quantize_fp8_prescaled.restype = st
         L.msamp_dequantize_fp8.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp]
         L.msamp_dequantize_fp8.restype = st
         L.msamp_adamw_o2_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
@@ -106,6 +109,8 @@ def lib():
         L.msamp_adam_o2_step.restype = st
         L.msamp_adam_o3_step.argtypes = L.msamp_adamw_o3_step.argtypes
         L.msamp_adam_o3_step.restype = st
+        L.msamp_adamw_o2_step_delayed.argtypes = L.msamp_adamw_o2_step.argtypes
+        L.msamp_adamw_o2_step_delayed.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -237,6 +242,19 @@ def quantize_fp8(x, fmt: int, meta: torch.Tensor, q) -> None:
                                     _stream(x.device)))
 
 
+def quantize_fp8_prescaled(x, fmt: int, meta: torch.Tensor, world_size: int, q) -> None:
+    """Pre-scaled quantize before an FP8 all-reduce over world_size ranks:
+    meta[t, 0] holds the common amax; scale = scale(amax * world_size)."""
+    x = _tl(x, "f32", "x")
+    q = _tl(q, "u8", "q")
+    x.matches(q, "q")
+    if x.n == 0:
+        return
+    _check(lib().msamp_quantize_fp8_prescaled(x.n, x.ptrs, x.numel, int(fmt),
+                                              _meta_ptr(meta, x.n, x.device, "meta"),
+                                              int(world_size), q.ptrs, _stream(x.device)))
+
+
 def dequantize_fp8(q, fmt: int, meta: torch.Tensor, out) -> None:
     """out[t] <- decode(q[t]) * meta[t, 2]."""
     q = _tl(q, "u8", "q")
@@ -299,6 +317,12 @@ def adam_o3_step(*args, **kw) -> None:
     """One in-place Adam (coupled L2) step in the O3 layout; arguments as
     adamw_o3_step (see msamp_adam_o3_step in include/msamp.h)."""
     adamw_o3_step(*args, _entry="msamp_adam_o3_step", **kw)
+
+
+def adamw_o2_step_delayed(*args, **kw) -> None:
+    """ABLATION: one-pass O2 AdamW step with delayed scaling of the first
+    moment (see msamp_adamw_o2_step_delayed in include/msamp.h)."""
+    adamw_o2_step(*args, _entry="msamp_adamw_o2_step_delayed", **kw)
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:

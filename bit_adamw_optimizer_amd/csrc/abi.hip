@@ -417,6 +417,36 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   return MSAMP_OK;
 }
 
+// Ablation: one-pass O2 step with delayed scaling of the first moment.
+msamp_status step_delayed_impl(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                               int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
+                               msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                               uint16_t* const* weight, const msamp_adamw_hparams* hp,
+                               int64_t step, void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
+  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
+  hipStream_t s = (hipStream_t)stream_ptr;
+  const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
+                                 (const void* const*)exp_avg_sq, (const void* const*)weight};
+  Plan* p = nullptr;
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p));
+  const StepConsts k = make_consts(hp, step, false);
+  MSAMP_LAUNCH(MSAMP_KERNEL_O2_DELAYED, s,
+               launch_step_delayed(grad_fmt, false, p->desc, p->chunks, p->nchunks, grad_meta,
+                                   exp_avg_meta, p->scratch_a, k, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_delayed_finalize(n, p->scratch_a, exp_avg_meta, s));
+  return MSAMP_OK;
+}
+
 template <typename F>
 msamp_status guarded(F&& f) {
   try {
@@ -452,6 +482,7 @@ const char* msamp_kernel_name(msamp_kernel_kind kind) {
     case MSAMP_KERNEL_O3_PASS3: return "o3_pass3";
     case MSAMP_KERNEL_FINALIZE: return "finalize";
     case MSAMP_KERNEL_AMAX_FINALIZE: return "amax_finalize";
+    case MSAMP_KERNEL_O2_DELAYED: return "o2_delayed";
     default: return "";
   }
 }
@@ -474,12 +505,13 @@ msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel, 
   });
 }
 
-msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t* numel,
-                                msamp_fp8_format fmt, msamp_meta* meta, uint8_t* const* q,
-                                void* stream) {
+static msamp_status quantize_impl(int32_t n, const float* const* x, const int64_t* numel,
+                                  msamp_fp8_format fmt, msamp_meta* meta, int32_t world,
+                                  uint8_t* const* q, void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
     MSAMP_TRY(check_common(n, numel));
+    if (world < 1) return fail(MSAMP_E_INVALID_ARG, "world_size must be >= 1");
     if (n == 0) return MSAMP_OK;
     MSAMP_TRY(check_fmt((int)fmt));
     MSAMP_TRY(check_list(n, numel, (const void* const*)x, "x"));
@@ -490,9 +522,21 @@ msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t*
     Plan* p = nullptr;
     MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, 2, true, s, &p));
     MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE, s,
-                 launch_quantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, s));
+                 launch_quantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, world, s));
     return MSAMP_OK;
   });
+}
+
+msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t* numel,
+                                msamp_fp8_format fmt, msamp_meta* meta, uint8_t* const* q,
+                                void* stream) {
+  return quantize_impl(n, x, numel, fmt, meta, 1, q, stream);
+}
+
+msamp_status msamp_quantize_fp8_prescaled(int32_t n, const float* const* x, const int64_t* numel,
+                                          msamp_fp8_format fmt, msamp_meta* meta,
+                                          int32_t world_size, uint8_t* const* q, void* stream) {
+  return quantize_impl(n, x, numel, fmt, meta, world_size, q, stream);
 }
 
 msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int64_t* numel,
@@ -559,6 +603,17 @@ msamp_status msamp_adam_o3_step(int32_t n, const int64_t* numel, const uint8_t* 
   return guarded([&]() {
     return step_impl(true, true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                      exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adamw_o2_step_delayed(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                         msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_delayed_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                             exp_avg_sq, weight, hp, step, stream);
   });
 }
 

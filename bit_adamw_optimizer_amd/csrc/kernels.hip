@@ -208,9 +208,9 @@ __global__ __launch_bounds__(kBlock) void k_amax_finalize(int32_t n, uint32_t* _
 template <int FMT>
 __global__ __launch_bounds__(kBlock) void k_quantize(const TensorDesc* __restrict__ desc,
                                                      const ChunkRef* __restrict__ chunks,
-                                                     msamp_meta* __restrict__ meta) {
+                                                     msamp_meta* __restrict__ meta, float world) {
   const ChunkRange r = chunk_range(chunks, desc);
-  const float s = scale_rule(meta[r.t].amax, Fp8Traits<FMT>::kMax);
+  const float s = scale_rule(meta[r.t].amax * world, Fp8Traits<FMT>::kMax);
   if (chunks[blockIdx.x].chunk == 0 && threadIdx.x == 0) {
     meta[r.t].scale = s;
     meta[r.t].scale_inv = 1.0f / s;
@@ -357,7 +357,11 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
 // Pass 2: recompute m1 exactly as in pass 1, then v1, w1; store m (E4M3 with
 // the new scale), v and w (FP16). In the O3 layout the weight is the master
 // and the amax of the stored master is reduced into amax_w.
-template <int GF, bool O3, bool COUPLED>
+//
+// DELAYED (an ablation of the two-pass scheme, O2 only): the codes are
+// encoded with the scale of the previous step's amax (mmeta.amax) and the
+// amax of the new m1 is reduced into amax_w for the next step.
+template <int GF, bool O3, bool COUPLED, bool DELAYED = false>
 __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
@@ -365,10 +369,13 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
                                                        const uint32_t* __restrict__ amax_m,
                                                        uint32_t* __restrict__ amax_w,
                                                        StepConsts k) {
+  static_assert(!(O3 && DELAYED), "the delayed-scaling ablation is O2 only");
   const ChunkRange r = chunk_range(chunks, desc);
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
-  const float s_m = scale_rule(__uint_as_float(amax_m[r.t]), kE4M3Max);
+  const float s_m = DELAYED ? scale_rule(mmeta[r.t].amax, kE4M3Max)
+                            : scale_rule(__uint_as_float(amax_m[r.t]), kE4M3Max);
+  uint32_t mmax = 0u;  // DELAYED: magnitude bits of the new first moment
   const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
   GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
   GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
@@ -396,6 +403,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
         const float m1 = first_moment(k, ge, m[e] * msi);
         float v1, w1;
         second_moment_and_weight(k, ge, m1, v[e], w[e], v1, w1);
+        if (DELAYED) mmax = umax(mmax, abs_bits(m1));
         m[e] = m1 * s_m;
         v[e] = v1;
         w[e] = w1;
@@ -422,6 +430,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
           const float m1 = first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi);
           float v1, w1;
           second_moment_and_weight(k, ge, m1, h_to_f(vh[i]), w0, v1, w1);
+          if (DELAYED) mmax = umax(mmax, abs_bits(m1));
           float mm[4] = {m1 * s_m, 0.0f, 0.0f, 0.0f};
           mq[i] = (uint8_t)(enc4<kE4M3>(mm) & 0xFFu);
           vh[i] = f_to_h(v1);
@@ -438,6 +447,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
     const uint32_t bits = abs_bits(h_to_f((uint16_t)wmax));
     block_max_into(bits, &amax_w[r.t]);
   }
+  if (DELAYED) block_max_into(mmax, &amax_w[r.t]);
 }
 
 // Pass 3 (O3): FP8 E4M3 copy of the stored master with its own scale.
@@ -500,6 +510,20 @@ __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* _
   }
 }
 
+__global__ __launch_bounds__(kBlock) void k_delayed_finalize(int32_t n, uint32_t* __restrict__ amax_new,
+                                                             msamp_meta* __restrict__ meta) {
+  const int32_t t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= n) return;
+  const float s = scale_rule(meta[t].amax, kE4M3Max);  // the scale the step encoded with
+  msamp_meta m;
+  m.amax = __uint_as_float(amax_new[t]);
+  m.scale = s;
+  m.scale_inv = 1.0f / s;
+  m.reserved = 0.0f;
+  meta[t] = m;
+  amax_new[t] = 0u;
+}
+
 // --------------------------------------------------------- codec probe ---
 
 __global__ __launch_bounds__(kBlock) void k_codec_probe(int op, const void* __restrict__ in,
@@ -558,12 +582,13 @@ hipError_t launch_amax_finalize(int32_t n, uint32_t* scratch, msamp_meta* meta,
 }
 
 hipError_t launch_quantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
-                           int64_t nchunks, msamp_meta* meta, hipStream_t stream) {
+                           int64_t nchunks, msamp_meta* meta, int32_t world, hipStream_t stream) {
   if (nchunks <= 0) return hipSuccess;
+  const float wf = (float)world;
   if (fmt == kE4M3)
-    k_quantize<kE4M3><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, meta);
+    k_quantize<kE4M3><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, meta, wf);
   else
-    k_quantize<kE5M2><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, meta);
+    k_quantize<kE5M2><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, meta, wf);
   return hipGetLastError();
 }
 
@@ -630,6 +655,32 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
     pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
   else
     pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
+                               int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                               uint32_t* amax_new, const StepConsts& k, hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  const unsigned g = grid_of(nchunks);
+  if (gfmt == kE4M3) {
+    if (coupled)
+      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+    else
+      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+  } else {
+    if (coupled)
+      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+    else
+      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* meta,
+                                   hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  k_delayed_finalize<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(n, amax_new, meta);
   return hipGetLastError();
 }
 

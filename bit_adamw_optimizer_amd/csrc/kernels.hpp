@@ -54,8 +54,10 @@ hipError_t launch_amax(const TensorDesc* desc, const ChunkRef* chunks, int64_t n
                        uint32_t* scratch, hipStream_t stream);
 hipError_t launch_amax_finalize(int32_t n, uint32_t* scratch, msamp_meta* meta,
                                 hipStream_t stream);
+// scale = scale_rule(meta.amax * world) (world = 1: the plain per-tensor
+// scale; world > 1: the pre-scale of an FP8 all-reduce over 'world' ranks).
 hipError_t launch_quantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
-                           int64_t nchunks, msamp_meta* meta, hipStream_t stream);
+                           int64_t nchunks, msamp_meta* meta, int32_t world, hipStream_t stream);
 hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* meta, hipStream_t stream);
 // 'coupled' selects Adam (L2 term wd*w added to the gradient before the
@@ -67,6 +69,16 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                              const StepConsts& k, hipStream_t stream);
+// Ablation: the O2 update in one pass with delayed scaling of the first
+// moment (encode with scale(mmeta.amax) of the previous step; reduce the new
+// amax into amax_new).
+hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
+                               int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                               uint32_t* amax_new, const StepConsts& k, hipStream_t stream);
+// meta[t] <- {amax_new[t], s, 1/s} with s = scale(meta[t].amax) (the scale
+// the delayed step used), then amax_new[t] <- 0.
+hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* meta,
+                                   hipStream_t stream);
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
                            const uint32_t* amax_w, hipStream_t stream);
 // meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then

@@ -139,6 +139,20 @@ msamp_status msamp_quantize_fp8(int32_t n, const float* const* x, const int64_t*
                                 void* stream);
 
 /*
+ * msamp_quantize_fp8_prescaled -- the quantize before an FP8 gradient
+ * all-reduce over world_size ranks ([OL] O1: FP8 weight gradients and FP8
+ * all-reduce). meta[t].amax must hold the common amax of tensor t over all
+ * ranks (the caller's all-reduce MAX of the per-rank msamp_amax results);
+ * the scale is scale(amax * world_size) with the product rounded to
+ * binary32, so the sum of the ranks' values stays within the FP8 range.
+ * world_size >= 1 (1 is msamp_quantize_fp8). Other arguments, outputs and
+ * errors as msamp_quantize_fp8.
+ */
+msamp_status msamp_quantize_fp8_prescaled(int32_t n, const float* const* x, const int64_t* numel,
+                                          msamp_fp8_format fmt, msamp_meta* meta,
+                                          int32_t world_size, uint8_t* const* q, void* stream);
+
+/*
  * msamp_dequantize_fp8 -- out = decode(q) * meta.scale_inv (binary32).
  *   q[t]      device uint8[numel[t]]
  *   meta[t]   device, read
@@ -214,6 +228,22 @@ msamp_status msamp_adam_o3_step(int32_t n, const int64_t* numel, const uint8_t* 
                                 uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                 const msamp_adamw_hparams* hp, int64_t step, void* stream);
 
+/*
+ * msamp_adamw_o2_step_delayed -- ABLATION, not the step defined above: the
+ * O2 AdamW step in one pass (11 bytes per element) with delayed scaling of
+ * the first moment. The new codes are encoded with s = scale(exp_avg_meta
+ * .amax) taken from the previous step, and exp_avg_meta becomes {amax of the
+ * new moment, s, 1/s}. At step 1 the scale is 1 and the moment (~1e-4 at
+ * gradient scale 1e-3) is stored as +-0; a moment that grows past 448/s
+ * saturates. It exists to measure what the second pass costs and what it
+ * buys. Arguments, layouts and errors as msamp_adamw_o2_step.
+ */
+msamp_status msamp_adamw_o2_step_delayed(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                         msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
 /* Frees every cached device table of the library (all devices) after
  * waiting for the devices to finish. Safe to call at any time from one
  * thread while no other library call runs. */
@@ -255,7 +285,8 @@ typedef enum {
   MSAMP_KERNEL_O3_PASS3 = 6,    /* O3 FP8 weight copy */
   MSAMP_KERNEL_FINALIZE = 7,    /* per-tensor meta write-back of a step */
   MSAMP_KERNEL_AMAX_FINALIZE = 8, /* amax write-back of msamp_amax */
-  MSAMP_KERNEL_COUNT = 9
+  MSAMP_KERNEL_O2_DELAYED = 9,  /* one-pass delayed-scaling ablation */
+  MSAMP_KERNEL_COUNT = 10
 } msamp_kernel_kind;
 
 /* on != 0 starts recording (and discards earlier records); on == 0 stops. */

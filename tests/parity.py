@@ -79,10 +79,11 @@ def u32(a) -> np.ndarray:
 class GpuState:
     """Device state of one workload, driven through the C ABI."""
 
-    def __init__(self, w: W.Workload, device, adam: bool = False):
+    def __init__(self, w: W.Workload, device, adam: bool = False, delayed: bool = False):
         self.w = w
         self.device = device
         self.adam = adam  # Adam (coupled L2) instead of AdamW
+        self.delayed = delayed  # one-pass delayed-scaling ablation (O2 AdamW)
         self.weights = W.init_weights(w, device)  # FP16 weight (O2) or master (O3)
         st = M.allocate_state(self.weights, w.level)
         self.exp_avg = st["exp_avg"]
@@ -109,7 +110,10 @@ class GpuState:
         w = self.w
         M.amax(self.tl_g32, self.grad_meta)
         M.quantize_fp8(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq)
-        if w.level == "O2":
+        if w.level == "O2" and self.delayed:
+            M.adamw_o2_step_delayed(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m,
+                                    self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
+        elif w.level == "O2":
             fn = M.adam_o2_step if self.adam else M.adamw_o2_step
             fn(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
                self.tl_v, self.tl_w, step=step, **w.hparams())
@@ -127,15 +131,15 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda",
-               adam: bool = False):
+               adam: bool = False, delayed: bool = False):
     """Runs 'steps' steps on the GPU and on the oracle (for the tensors in
     'verify', default all) and returns a dict of Stats per output. adam=True
     runs the Adam (coupled L2) entry points instead of AdamW."""
     verify = list(range(w.n)) if verify is None else list(verify)
     t0 = time.time()
-    gs = GpuState(w, device, adam=adam)
+    gs = GpuState(w, device, adam=adam, delayed=delayed)
     torch.cuda.synchronize()
-    ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam) for t in verify}
+    ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam, delayed=delayed) for t in verify}
     stats = {k: Stats() for k in ("m", "v", "w", "w8", "m_meta", "w8_meta")}
     pool = ThreadPoolExecutor(max_workers=threads)
     hp = w.hparams()

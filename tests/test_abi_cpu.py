@@ -93,6 +93,8 @@ def test_other_entry_points_validate():
     assert L.msamp_dequantize_fp8(1, _vp(0), _i64(4), 0, ctypes.c_void_p(0x2000), _vp(0x3000), None) == 1
     assert L.msamp_codec_probe(9, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 4, None) == 1
     assert L.msamp_codec_probe(0, ctypes.c_void_p(0x1001), ctypes.c_void_p(0x2000), 4, None) == 2
+    assert L.msamp_quantize_fp8_prescaled(1, _vp(0x1000), _i64(4), 0, ctypes.c_void_p(0x2000), 0,
+                                          _vp(0x3000), None) == 1
     assert L.msamp_kernel_name(4) == b"o2_pass2"
     assert L.msamp_kernel_name(99) == b""
 

@@ -130,3 +130,34 @@ def test_misaligned_and_invalid_arguments_enqueue_nothing():
     assert torch.equal(meta, before)
     # n = 0 is a no-op
     M.amax([], M.new_meta(0, DEV))
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_prescaled_quantize_matches_oracle(fmt):
+    """O1 pre-scale (common amax of N ranks, scale(amax * N)): N emulated
+    ranks on one GPU, the common amax taken as the max of their msamp_amax
+    results, each quantized with world_size = N; bit-exact against the
+    oracle."""
+    log("prescaled fmt=%d" % fmt)
+    rng = np.random.default_rng(33 + fmt)
+    for world in (1, 2, 6, 8):
+        ranks = [_tensors(rng, [70_001], specials=False)[0] for _ in range(world)]
+        metas = [M.new_meta(1, DEV) for _ in range(world)]
+        dx = [_to_dev([r]) for r in ranks]
+        for d, m in zip(dx, metas):
+            M.amax(d, m)
+        torch.cuda.synchronize()
+        common = max(float(m[0, 0]) for m in metas)
+        q = []
+        for d, m in zip(dx, metas):
+            m[0, 0] = common
+            qq = [torch.empty(70_001, dtype=torch.uint8, device=DEV)]
+            M.quantize_fp8_prescaled(d, fmt, m, world, qq)
+            q.append(qq[0])
+        torch.cuda.synchronize()
+        for r, m, qq in zip(ranks, metas, q):
+            qr, mr = O.quantize_fp8_prescaled(r, fmt, common, world)
+            assert np.array_equal(qq.cpu().numpy(), qr)
+            assert np.array_equal(u32(m[0, :3].cpu().numpy()), u32(mr[:3]))
+    with pytest.raises(M.MsampError):
+        M.quantize_fp8_prescaled(dx[0], fmt, metas[0], 0, q[:1])

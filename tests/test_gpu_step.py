@@ -79,6 +79,22 @@ def test_adam_ragged_e5m2():
     assert_bar(stats)
 
 
+def test_delayed_scaling_ablation_10_steps():
+    """One-pass delayed-scaling O2 step (an ablation entry point): parity with
+    the oracle's ablation, and its step-1 failure (first moment stored as
+    +-0) on the GPU."""
+    # gradients ~ N(0, 1e-3): |m1| = 0.1|g| stays below half the smallest
+    # E4M3 subnormal (2^-10), so with scale 1 every code is +-0
+    w1 = W.make("single_1m")
+    stats, gs, _ = run_parity(w1, 1, delayed=True)
+    assert_bar(stats)
+    assert ((host(gs.exp_avg[0]) & 0x7F) == 0).all()
+    w = W.make("tiny_llama")
+    stats, _, _ = run_parity(w, 10, delayed=True)
+    _report("delayed", stats)
+    assert_bar(stats)
+
+
 def test_ragged_sizes_o2_and_o3():
     """Sizes around the 16-element vector, the 4096-element tile and the
     65536-element chunk, including empty tensors."""
