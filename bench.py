@@ -189,17 +189,28 @@ def cpu_baseline(w, device, threads: int) -> dict:
                                                          sub.params, w.level)}
 
 
-# rocprofv3 kernel names of the library's kernels -> profile kernel kinds
-KERNEL_SYMBOLS = {"k_amax(": "amax", "k_quantize<": "quantize_fp8", "k_step_pass1<": "step_pass1",
-                  "k_step_pass2<0, false>": "o2_pass2", "k_step_pass2<1, false>": "o2_pass2",
-                  "k_step_pass2<0, true>": "o3_pass2", "k_step_pass2<1, true>": "o3_pass2",
-                  "k_o3_pass3(": "o3_pass3"}
-
-
 def _kind_of(name: str):
-    for sym, kind in KERNEL_SYMBOLS.items():
-        if "msamp::" in name and sym in name:
-            return kind
+    """(kernel kind, algorithmic bytes per parameter) of one of the library's
+    kernels from its rocprofv3 name (template arguments included), or None."""
+    if "msamp::" not in name:
+        return None
+    m = re.search(r"\b(k_\w+)(?:<([^>]*)>)?\(", name)
+    if not m:
+        return None
+    fn, targs = m.group(1), [a.strip() for a in (m.group(2) or "").split(",") if a.strip()]
+    if fn == "k_amax":
+        return "amax", GRAD_AMAX_BYTES
+    if fn == "k_quantize":
+        return "quantize_fp8", GRAD_QUANTIZE_BYTES
+    if fn == "k_step_pass1":  # <grad format, coupled>
+        coupled = len(targs) > 1 and targs[1] == "true"
+        return "step_pass1", PASS1_BYTES + (2 if coupled else 0)
+    if fn == "k_step_pass2":  # <grad format, O3, coupled[, delayed]>
+        if len(targs) > 3 and targs[3] == "true":
+            return "o2_delayed", PASS2_BYTES
+        return ("o3_pass2" if len(targs) > 1 and targs[1] == "true" else "o2_pass2"), PASS2_BYTES
+    if fn == "k_o3_pass3":
+        return "o3_pass3", PASS3_BYTES
     return None
 
 
@@ -256,8 +267,6 @@ def summarize_profiles(dirs, workload: str) -> None:
 
     from bit_adamw_optimizer_amd import workloads as W
     w = W.make(workload)
-    per_param = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES, "step_pass1": PASS1_BYTES,
-                 "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES, "o3_pass3": PASS3_BYTES}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     lines = ["# HBM traffic per launch, %s (%d params), from rocprofv3 counters" % (workload, w.params), "",
              "Commands (run from the repository root; R=$PWD; cd /tmp first):",
@@ -279,13 +288,14 @@ def summarize_profiles(dirs, workload: str) -> None:
              "|---|---|---|---|---|---|---|"]
     out = {}
     for name in sorted(set(fetch) | set(write)):
-        kind = _kind_of(name)
-        if kind is None:
+        kb = _kind_of(name)
+        if kb is None:
             continue
+        kind, bpp = kb
         f = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [0])))
         wr = sum(write.get(name, [0])) / max(1, len(write.get(name, [0])))
         hbm = f * 1024 * ffac + wr * 1024 * wfac
-        alg = per_param[kind] * w.params
+        alg = bpp * w.params
         out[kind] = {"fetch_kib": f, "write_kib": wr, "hbm_bytes_per_launch": hbm, "algorithmic_bytes": alg}
         lines.append("| %s | %d | %.1f | %.1f | %.4g | %.4g | %.4f |"
                      % (kind, len(fetch.get(name, [])), f, wr, hbm, alg, hbm / alg))
@@ -303,13 +313,13 @@ def summarize_profiles(dirs, workload: str) -> None:
               "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline" % workload, "",
               "| kernel | calls | average ms | min ms | max ms | algorithmic GB/s (avg) |", "|---|---|---|---|---|---|"]
         for r in rows:
-            kind = _kind_of(r["Name"])
-            if kind is None and "msamp::" not in r["Name"]:
+            if "msamp::" not in r["Name"]:
                 continue
+            kb = _kind_of(r["Name"])
             avg = float(r["AverageNs"]) * 1e-6
-            gbps = per_param[kind] * w.params / (avg * 1e-3) / 1e9 if kind in per_param else float("nan")
+            gbps = kb[1] * w.params / (avg * 1e-3) / 1e9 if kb else float("nan")
             m = re.search(r"\b(k_\w+)", r["Name"])
-            short = kind or (m.group(1) if m else r["Name"][:40])
+            short = kb[0] if kb else (m.group(1) if m else r["Name"][:40])
             tl.append("| %s | %s | %.4f | %.4f | %.4f | %.1f |" % (short, r["Calls"], avg,
                       float(r["MinNs"]) * 1e-6, float(r["MaxNs"]) * 1e-6, gbps))
         with open(os.path.join(ROOT, "profiles", "path_kernels_%s_kernel_trace.md" % workload), "w") as fh:
