@@ -95,6 +95,8 @@ def lib():
         L.oracle_adamw_o3_tensor.restype = i32
         L.oracle_adamw_o2_tensor_delayed.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, hp, i64, i32]
         L.oracle_adamw_o2_tensor_delayed.restype = i32
+        L.oracle_adamw_o2_tensor_scaled_v.argtypes = [i64, vp, i32, f32, vp, vp, vp, vp, vp, hp, i64]
+        L.oracle_adamw_o2_tensor_scaled_v.restype = i32
         _lib = L
     return _lib
 
@@ -238,6 +240,19 @@ def adamw_o2_tensor_delayed(qg, gfmt, g_scale_inv, qm, m_meta, v, w, step: int, 
         raise RuntimeError("oracle_adamw_o2_tensor_delayed failed (%d)" % rc)
 
 
+def adamw_o2_tensor_scaled_v(qg, gfmt, g_scale_inv, qm, m_meta, v, v_meta, w, step: int, **hp) -> None:
+    """Ablation: O2 step with a per-tensor-scaled FP16 second moment (v_meta:
+    float32[4] {amax, scale, scale_inv, 0} of the stored v)."""
+    assert v_meta.dtype == np.float32 and v_meta.size >= 3
+    qg = np.ascontiguousarray(qg, dtype=np.uint8)
+    h = _hp(**hp)
+    rc = lib().oracle_adamw_o2_tensor_scaled_v(qg.size, _ptr(qg), gfmt, float(np.float32(g_scale_inv)),
+                                               _ptr(qm), _ptr(m_meta), _ptr(v), _ptr(v_meta), _ptr(w),
+                                               ctypes.byref(h), int(step))
+    if rc != 0:
+        raise RuntimeError("oracle_adamw_o2_tensor_scaled_v failed (%d)" % rc)
+
+
 def adamw_o3_tensor(qg, gfmt, g_scale_inv, qm, m_meta, v, master, w8, w8_meta, step: int,
                     adam: bool = False, **hp) -> None:
     """One O3 step on one tensor, in place on qm, m_meta, v, master (FP16
@@ -258,12 +273,14 @@ class TensorState:
     """Host copy of one tensor's low-precision optimizer state."""
 
     def __init__(self, weight_f16_bits: np.ndarray, level: str = "O2", adam: bool = False,
-                 delayed: bool = False):
+                 delayed: bool = False, scaled_v: bool = False):
         n = weight_f16_bits.size
         self.level = level
         self.adam = adam  # Adam with coupled L2 instead of AdamW
         self.delayed = delayed  # one-pass delayed-scaling ablation (O2 only)
-        assert not (delayed and level != "O2")
+        self.scaled_v = scaled_v  # scaled-FP16-v ablation (O2 AdamW only)
+        assert not ((delayed or scaled_v) and level != "O2")
+        self.v_meta = np.array([0.0, 1.0, 1.0, 0.0], np.float32)
         self.w = np.ascontiguousarray(weight_f16_bits, dtype=np.uint16).copy()  # weight or master
         self.m = np.zeros(n, np.uint8)
         self.m_meta = np.array([0.0, 1.0, 1.0, 0.0], np.float32)
@@ -277,7 +294,10 @@ def step_tensor(state: TensorState, grad_f32: np.ndarray, gfmt: int, step: int, 
     """Gradient amax + quantize, then one O2/O3 step of one tensor's state.
     Returns the gradient (codes, meta)."""
     qg, gmeta = quantize_fp8(grad_f32, gfmt)
-    if state.level == "O2" and state.delayed:
+    if state.level == "O2" and state.scaled_v:
+        adamw_o2_tensor_scaled_v(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.v_meta,
+                                 state.w, step, **hp)
+    elif state.level == "O2" and state.delayed:
         adamw_o2_tensor_delayed(qg, gfmt, gmeta[2], state.m, state.m_meta, state.v, state.w, step,
                                 adam=state.adam, **hp)
     elif state.level == "O2":

@@ -496,6 +496,60 @@ int oracle_adamw_o2_tensor_delayed(int64_t n, const uint8_t* qg, int gfmt, float
   return 0;
 }
 
+/* Ablation (not the reading the step follows, see R-FP32 / the flagged FP16
+ * underflow of v): the O2 step with a per-tensor-scaled FP16 second moment.
+ * v is stored as fp16(v1 * s_v) with s_v = scale(amax(v1), 65504) and its
+ * own meta {amax_v, s_v, 1/s_v}; v0 = f32(code) * v_meta[2] (old 1/s_v).
+ * Both amaxes come from the first pass (which therefore also reads v), the
+ * second pass recomputes m1 and v1 identically and stores everything. */
+int oracle_adamw_o2_tensor_scaled_v(int64_t n, const uint8_t* qg, int gfmt, float g_scale_inv,
+                                    uint8_t* qm, float* m_meta, uint16_t* v, float* v_meta,
+                                    uint16_t* w, const oracle_hparams* hp, int64_t step) {
+  const mf_format* gf = fp8_format(gfmt);
+  if (!gf) return -1;
+  float k[K_COUNT];
+  oracle_adamw_constants(hp, step, k);
+  float m_si_old = m_meta[2], v_si_old = v_meta[2];
+  float* g = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  float* m1 = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  float* v1 = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+  if (!g || !m1 || !v1) {
+    free(g);
+    free(m1);
+    free(v1);
+    return -1;
+  }
+  uint32_t am = 0u, av = 0u;
+  for (int64_t i = 0; i < n; ++i) {
+    g[i] = fp8_dec(gf, qg[i]) * g_scale_inv;
+    m1[i] = adamw_first_moment(k, g[i], fp8_dec(&FMT_E4M3, qm[i]) * m_si_old);
+    v1[i] = fmaf(k[K_B2], f16_dec(v[i]) * v_si_old, k[K_OB2] * (g[i] * g[i]));
+    uint32_t u = f32_bits(m1[i]) & 0x7FFFFFFFu;
+    if (u > am) am = u;
+    u = f32_bits(v1[i]) & 0x7FFFFFFFu;
+    if (u > av) av = u;
+  }
+  float s_m = oracle_scale(f32_from_bits(am), (float)mf_max(&FMT_E4M3));
+  float s_v = oracle_scale(f32_from_bits(av), (float)mf_max(&FMT_F16));
+  for (int64_t i = 0; i < n; ++i) {
+    float den = fmaf(sqrtf(v1[i]), k[K_IBS], k[K_EPS]);
+    float w1 = fmaf(-k[K_SS], m1[i] / den, f16_dec(w[i]) * k[K_DEC]);
+    w[i] = f16_enc(w1);
+    v[i] = f16_enc(v1[i] * s_v);
+    qm[i] = fp8_enc(&FMT_E4M3, m1[i] * s_m);
+  }
+  m_meta[0] = f32_from_bits(am);
+  m_meta[1] = s_m;
+  m_meta[2] = 1.0f / s_m;
+  v_meta[0] = f32_from_bits(av);
+  v_meta[1] = s_v;
+  v_meta[2] = 1.0f / s_v;
+  free(g);
+  free(m1);
+  free(v1);
+  return 0;
+}
+
 /* O3 step on one tensor (coupled = 1: Adam): the O2 update applied to the
  * FP16 master weight,
  * then the FP8 E4M3 regular-weight copy from the stored master (R-O3COPY):

@@ -339,6 +339,67 @@ def test_delayed_scaling_ablation_matches_exact_arithmetic_and_zeroes_m_at_step_
     assert ((ost.m & 0x7F) == 0x7E).sum() >= 1
 
 
+def exact_step_scaled_v(state, g32, gfmt, step, hp=HP):
+    """Exact-rational reference of the scaled-FP16-v ablation."""
+    B1, OB1, B2, OB2, EPS, SS, IBS, DEC, WD = exact_constants(step, **hp)
+    amax_g = max(float_to_bits(float(x)) & 0x7FFFFFFF for x in g32)
+    s_g = exact_scale(F(amax_g), O.fp8_max(gfmt))
+    si_g = F.of(1.0) / s_g
+    gs, m1s, v1s = [], [], []
+    for i, x in enumerate(g32):
+        xs = F.of(float(x)) * s_g
+        g = fp8_value(brute_encode_fp8(xs.q, gfmt, bool(xs.b >> 31)), gfmt) * si_g
+        m1 = F.fma(B1, fp8_value(state["m"][i], 0) * state["m_si"], OB1 * g)
+        v1 = F.fma(B2, f16_value(state["v"][i]) * state["v_si"], OB2 * (g * g))
+        gs.append(g); m1s.append(m1); v1s.append(v1)
+    am = F(max(m.b & 0x7FFFFFFF for m in m1s))
+    av = F(max(v.b & 0x7FFFFFFF for v in v1s))
+    s_m, s_v = exact_scale(am, 448.0), exact_scale(av, 65504.0)
+    for i in range(len(g32)):
+        den = F.fma(v1s[i].sqrt(), IBS, EPS)
+        w1 = F.fma(-SS, m1s[i] / den, f16_value(state["w"][i]) * DEC)
+        state["w"][i] = brute_encode_f16(w1.q, bool(w1.b >> 31))
+        vs = v1s[i] * s_v
+        state["v"][i] = brute_encode_f16(vs.q, bool(vs.b >> 31))
+        ms = m1s[i] * s_m
+        state["m"][i] = brute_encode_fp8(ms.q, 0, bool(ms.b >> 31))
+    state["m_si"] = F.of(1.0) / s_m
+    state["v_si"] = F.of(1.0) / s_v
+    return (am.b, s_m.b, state["m_si"].b), (av.b, s_v.b, state["v_si"].b)
+
+
+def test_scaled_v_ablation_matches_exact_arithmetic_and_keeps_v():
+    """Per-tensor-scaled FP16 second moment (an ablation of the literal
+    unscaled FP16 v): bit-exact against exact arithmetic over three steps; at
+    gradient scale 1e-3 the stored v is no longer +0, and it decodes to the
+    binary32 v1 within FP16 precision."""
+    rng = np.random.default_rng(13)
+    n = 6
+    w = list(O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32)))
+    ost = O.TensorState(np.array(w, np.uint16), "O2", scaled_v=True)
+    est = {"w": [int(x) for x in w], "v": [0] * n, "m": [0] * n, "m_si": F.of(1.0), "v_si": F.of(1.0)}
+    for t in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        O.step_list([ost], [g], O.E4M3, t, **HP)
+        mm, vm = exact_step_scaled_v(est, g, O.E4M3, t)
+        assert list(ost.m) == est["m"] and list(ost.v) == est["v"] and list(ost.w) == est["w"]
+        assert u32(ost.m_meta) == list(mm) and u32(ost.v_meta) == list(vm)
+    assert (ost.v != 0).all()
+    # large tensor: unscaled v underflows, scaled v keeps its values
+    n = 50_000
+    w16 = O.f16_encode((rng.standard_normal(n) * 0.02).astype(np.float32))
+    a = O.TensorState(w16, "O2", scaled_v=True)
+    b = O.TensorState(w16, "O2")
+    m = np.zeros(n, np.float32); v = np.zeros(n, np.float32); wf = O.f16_decode(w16)
+    for t in range(1, 4):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        O.step_list([a], [g], O.E4M3, t, **HP)
+        O.step_list([b], [g], O.E4M3, t, **HP)
+    assert (b.v == 0).mean() > 0.999 and (a.v == 0).mean() < 0.01
+    v_dec = O.f16_decode(a.v).astype(np.float64) * a.v_meta[2]
+    assert np.median(v_dec) > 1e-10
+
+
 def test_quantized_trajectory_tracks_fp32_trajectory():
     """O2 storage error only: after 10 steps w stays within the accumulated
     FP8-m / FP16 rounding of the binary32 AdamW trajectory."""
