@@ -57,9 +57,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama2_7b",
                    help="llama2_7b (default), llama2_13b, gpt2_small, single_1m, stress")
-    p.add_argument("--optimizer", default="adamw", choices=("adamw", "adam", "adamw-delayed"),
-                   help="adamw (decoupled decay, default), adam (coupled L2), or the one-pass "
-                        "delayed-scaling ablation adamw-delayed (O2 only)")
+    p.add_argument("--optimizer", default="adamw", choices=("adamw", "adam", "adamw-delayed", "adamw-scaled-v"),
+                   help="adamw (decoupled decay, default), adam (coupled L2), or the O2-only "
+                        "ablations adamw-delayed (one-pass delayed scaling) and adamw-scaled-v "
+                        "(per-tensor-scaled FP16 second moment)")
     p.add_argument("--shard", type=int, default=1,
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -91,7 +92,8 @@ def calibrate_copy(gib: float) -> None:
 class State:
     """Device state of a workload plus two resident binary32 gradient sets."""
 
-    def __init__(self, w, device, adam: bool = False, delayed: bool = False):
+    def __init__(self, w, device, adam: bool = False, delayed: bool = False,
+                 scaled_v: bool = False):
         import torch
 
         import bit_adamw_optimizer_amd as M
@@ -100,6 +102,8 @@ class State:
         self.w = w
         self.adam = adam
         self.delayed = delayed
+        self.scaled_v = scaled_v
+        self.exp_avg_sq_meta = M.new_meta(w.n, device) if scaled_v else None
         # every role lives in one allocation (views per tensor)
         self.weights = W.init_weights(w, device, out=M.flat_views(w.numel, torch.float16, device))
         st = M.allocate_state(self.weights, w.level, flat=True)
@@ -126,7 +130,11 @@ class State:
         g32 = self.grad_sets[(step - 1) % 2]
         M.amax(g32, self.grad_meta)
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
-        if w.level == "O2":
+        if w.level == "O2" and self.scaled_v:
+            M.adamw_o2_step_scaled_v(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m,
+                                     self.exp_avg_meta, self.tl_v, self.exp_avg_sq_meta, self.tl_w,
+                                     step=step, **w.hparams())
+        elif w.level == "O2":
             fn = M.adam_o2_step if self.adam else M.adamw_o2_step
             if self.delayed:
                 fn = M.adamw_o2_step_delayed
@@ -211,6 +219,10 @@ def _kind_of(name: str):
         return ("o3_pass2" if len(targs) > 1 and targs[1] == "true" else "o2_pass2"), PASS2_BYTES
     if fn == "k_o3_pass3":
         return "o3_pass3", PASS3_BYTES
+    if fn == "k_scaled_v_pass1":  # also reads the FP16 second moment
+        return "step_pass1", PASS1_BYTES + 2
+    if fn == "k_scaled_v_pass2":
+        return "o2_pass2", PASS2_BYTES
     return None
 
 
@@ -369,10 +381,11 @@ def main() -> int:
           file=sys.stderr, flush=True)
     adam = args.optimizer == "adam"
     delayed = args.optimizer == "adamw-delayed"
-    if delayed and w.level != "O2":
-        print("the delayed-scaling ablation exists for the O2 layout only", file=sys.stderr)
+    scaled_v = args.optimizer == "adamw-scaled-v"
+    if (delayed or scaled_v) and w.level != "O2":
+        print("the %s ablation exists for the O2 layout only" % args.optimizer, file=sys.stderr)
         return 2
-    st = State(w, device, adam=adam, delayed=delayed)
+    st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v)
 
     step = 0
     for _ in range(args.warmup):
@@ -400,7 +413,8 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     P = w.params
     # Adam's pass 1 also reads the FP16 weight for its L2 term
-    pass1_bytes = PASS1_BYTES + (2 if adam else 0)
+    # (and so does the scaled-v ablation's, for its amax(v1))
+    pass1_bytes = PASS1_BYTES + (2 if adam or scaled_v else 0)
     step_bytes = (0 if delayed else pass1_bytes) + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
     path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
     gbps = path_bytes * P / (ms_per_step * 1e-3) / 1e9
@@ -441,7 +455,9 @@ def main() -> int:
                                "(amax + quantize + step per iteration)"
                                % (w.name, w.level, {"adam": "Adam", "adamw": "AdamW",
                                                     "adamw-delayed": "AdamW one-pass delayed-scaling "
-                                                                     "ablation"}[args.optimizer],
+                                                                     "ablation",
+                                                    "adamw-scaled-v": "AdamW scaled-FP16-v "
+                                                                      "ablation"}[args.optimizer],
                                   w.n, P,
                                   "E4M3" if w.grad_fmt == 0 else "E5M2"),
                    "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P},

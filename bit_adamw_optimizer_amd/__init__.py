@@ -111,6 +111,9 @@ def lib():
         L.msamp_adam_o3_step.restype = st
         L.msamp_adamw_o2_step_delayed.argtypes = L.msamp_adamw_o2_step.argtypes
         L.msamp_adamw_o2_step_delayed.restype = st
+        L.msamp_adamw_o2_step_scaled_v.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.POINTER(_HParams), i64, vp]
+        L.msamp_adamw_o2_step_scaled_v.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -323,6 +326,27 @@ def adamw_o2_step_delayed(*args, **kw) -> None:
     """ABLATION: one-pass O2 AdamW step with delayed scaling of the first
     moment (see msamp_adamw_o2_step_delayed in include/msamp.h)."""
     adamw_o2_step(*args, _entry="msamp_adamw_o2_step_delayed", **kw)
+
+
+def adamw_o2_step_scaled_v(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
+                           exp_avg_sq_meta, weight, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
+                           weight_decay=0.01, step: int) -> None:
+    """ABLATION: O2 AdamW step with a per-tensor-scaled FP16 second moment
+    (see msamp_adamw_o2_step_scaled_v in include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    hp = _hp(lr, betas, eps, weight_decay)
+    _check(lib().msamp_adamw_o2_step_scaled_v(
+        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs,
+        _meta_ptr(exp_avg_sq_meta, g.n, g.device, "exp_avg_sq_meta"), w.ptrs,
+        ctypes.byref(hp), int(step), _stream(g.device)))
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:

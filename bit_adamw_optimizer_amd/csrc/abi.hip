@@ -413,7 +413,43 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
                  launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
   MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
-                                    o3 ? weight_fp8_meta : nullptr, s));
+                                    o3 ? weight_fp8_meta : nullptr, 448.0f, s));
+  return MSAMP_OK;
+}
+
+// Ablation: O2 AdamW step with a per-tensor-scaled FP16 second moment.
+msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
+                                msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                msamp_meta* exp_avg_sq_meta, uint16_t* const* weight,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
+  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_sq_meta, "exp_avg_sq_meta"));
+  hipStream_t s = (hipStream_t)stream_ptr;
+  const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
+                                 (const void* const*)exp_avg_sq, (const void* const*)weight};
+  Plan* p = nullptr;
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p));
+  const StepConsts k = make_consts(hp, step, false);
+  MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
+               launch_scaled_v_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
+                                     exp_avg_meta, exp_avg_sq_meta, p->scratch_a, p->scratch_b, k, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_O2_PASS2, s,
+               launch_scaled_v_pass2(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
+                                     exp_avg_meta, exp_avg_sq_meta, p->scratch_a, p->scratch_b, k, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+               launch_step_finalize(n, p->scratch_a, exp_avg_meta, p->scratch_b, exp_avg_sq_meta,
+                                    65504.0f, s));
   return MSAMP_OK;
 }
 
@@ -614,6 +650,18 @@ msamp_status msamp_adamw_o2_step_delayed(int32_t n, const int64_t* numel, const 
   return guarded([&]() {
     return step_delayed_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                              exp_avg_sq, weight, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, msamp_meta* exp_avg_sq_meta,
+                                          uint16_t* const* weight, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_scaled_v_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                              exp_avg_sq, exp_avg_sq_meta, weight, hp, step, stream);
   });
 }
 

@@ -483,7 +483,8 @@ __global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restric
 __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* __restrict__ amax_a,
                                                           msamp_meta* __restrict__ meta_a,
                                                           uint32_t* __restrict__ amax_b,
-                                                          msamp_meta* __restrict__ meta_b) {
+                                                          msamp_meta* __restrict__ meta_b,
+                                                          float fmax_b) {
   const int32_t t = blockIdx.x * kBlock + threadIdx.x;
   if (t >= n) return;
   {
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* _
   }
   if (meta_b != nullptr) {
     const float a = __uint_as_float(amax_b[t]);
-    const float s = scale_rule(a, kE4M3Max);
+    const float s = scale_rule(a, fmax_b);
     msamp_meta m;
     m.amax = a;
     m.scale = s;
@@ -507,6 +508,123 @@ __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* _
     m.reserved = 0.0f;
     meta_b[t] = m;
     amax_b[t] = 0u;
+  }
+}
+
+// ----------------------------------------- scaled-FP16-v ablation (O2) ---
+
+constexpr float kF16Max = 65504.0f;
+
+// Pass 1 of the scaled-v ablation: new first and second moments and both
+// per-tensor amaxes (v0 = f32(code) * old 1/s_v).
+template <int GF>
+__global__ __launch_bounds__(kBlock) void k_scaled_v_pass1(const TensorDesc* __restrict__ desc,
+                                                           const ChunkRef* __restrict__ chunks,
+                                                           const msamp_meta* __restrict__ gmeta,
+                                                           const msamp_meta* __restrict__ mmeta,
+                                                           const msamp_meta* __restrict__ vmeta,
+                                                           uint32_t* __restrict__ amax_m,
+                                                           uint32_t* __restrict__ amax_v,
+                                                           StepConsts k) {
+  const ChunkRange r = chunk_range(chunks, desc);
+  const float gsi = gmeta[r.t].scale_inv, msi = mmeta[r.t].scale_inv, vsi = vmeta[r.t].scale_inv;
+  const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
+  const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  const GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
+  uint32_t mx = 0u, vx = 0u;
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
+      float g[16], m[16], v[16];
+      dec8<GF>(load<u32x2>(gq + e0), g);
+      dec8<GF>(load<u32x2>(gq + e1), g + 8);
+      dec8<kE4M3>(load<u32x2>(mq + e0), m);
+      dec8<kE4M3>(load<u32x2>(mq + e1), m + 8);
+      h8_to_f8(load<u32x4>(vh + e0), v);
+      h8_to_f8(load<u32x4>(vh + e1), v + 8);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float ge = g[e] * gsi;
+        mx = umax(mx, abs_bits(first_moment(k, ge, m[e] * msi)));
+        vx = umax(vx, abs_bits(__builtin_fmaf(k.b2, v[e] * vsi, k.ob2 * (ge * ge))));
+      }
+    } else {
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          const float ge = dec1<GF>(gq[i]) * gsi;
+          mx = umax(mx, abs_bits(first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi)));
+          vx = umax(vx, abs_bits(__builtin_fmaf(k.b2, h_to_f(vh[i]) * vsi, k.ob2 * (ge * ge))));
+        }
+      }
+    }
+  }
+  block_max_into(mx, &amax_m[r.t]);
+  block_max_into(vx, &amax_v[r.t]);
+}
+
+// Pass 2 of the scaled-v ablation: recompute m1, v1 identically; store m
+// (E4M3, new scale), v = fp16(v1 * s_v) and w.
+template <int GF>
+__global__ __launch_bounds__(kBlock) void k_scaled_v_pass2(const TensorDesc* __restrict__ desc,
+                                                           const ChunkRef* __restrict__ chunks,
+                                                           const msamp_meta* __restrict__ gmeta,
+                                                           const msamp_meta* __restrict__ mmeta,
+                                                           const msamp_meta* __restrict__ vmeta,
+                                                           const uint32_t* __restrict__ amax_m,
+                                                           const uint32_t* __restrict__ amax_v,
+                                                           StepConsts k) {
+  const ChunkRange r = chunk_range(chunks, desc);
+  const float gsi = gmeta[r.t].scale_inv, msi = mmeta[r.t].scale_inv, vsi = vmeta[r.t].scale_inv;
+  const float s_m = scale_rule(__uint_as_float(amax_m[r.t]), kE4M3Max);
+  const float s_v = scale_rule(__uint_as_float(amax_v[r.t]), kF16Max);
+  const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
+  GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
+  GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
+      float g[16], m[16], v[16], w[16];
+      dec8<GF>(load<u32x2>(gq + e0), g);
+      dec8<GF>(load<u32x2>(gq + e1), g + 8);
+      dec8<kE4M3>(load<u32x2>(mq + e0), m);
+      dec8<kE4M3>(load<u32x2>(mq + e1), m + 8);
+      h8_to_f8(load<u32x4>(vh + e0), v);
+      h8_to_f8(load<u32x4>(vh + e1), v + 8);
+      h8_to_f8(load<u32x4>(wh + e0), w);
+      h8_to_f8(load<u32x4>(wh + e1), w + 8);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float ge = g[e] * gsi;
+        const float m1 = first_moment(k, ge, m[e] * msi);
+        float v1, w1;
+        second_moment_and_weight(k, ge, m1, v[e] * vsi, w[e], v1, w1);
+        m[e] = m1 * s_m;
+        v[e] = v1 * s_v;
+        w[e] = w1;
+      }
+      store<u32x2>(mq + e0, enc8<kE4M3>(m));
+      store<u32x2>(mq + e1, enc8<kE4M3>(m + 8));
+      store<u32x4>(vh + e0, f8_to_h8(v));
+      store<u32x4>(vh + e1, f8_to_h8(v + 8));
+      store<u32x4>(wh + e0, f8_to_h8(w));
+      store<u32x4>(wh + e1, f8_to_h8(w + 8));
+    } else {
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          const float ge = dec1<GF>(gq[i]) * gsi;
+          const float m1 = first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi);
+          float v1, w1;
+          second_moment_and_weight(k, ge, m1, h_to_f(vh[i]) * vsi, h_to_f(wh[i]), v1, w1);
+          float mm[4] = {m1 * s_m, 0.0f, 0.0f, 0.0f};
+          mq[i] = (uint8_t)(enc4<kE4M3>(mm) & 0xFFu);
+          vh[i] = f_to_h(v1 * s_v);
+          wh[i] = f_to_h(w1);
+        }
+      }
+    }
   }
 }
 
@@ -677,6 +795,32 @@ hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, c
   return hipGetLastError();
 }
 
+hipError_t launch_scaled_v_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                                 const msamp_meta* vmeta, uint32_t* amax_m, uint32_t* amax_v,
+                                 const StepConsts& k, hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  const unsigned g = grid_of(nchunks);
+  if (gfmt == kE4M3)
+    k_scaled_v_pass1<kE4M3><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, vmeta, amax_m, amax_v, k);
+  else
+    k_scaled_v_pass1<kE5M2><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, vmeta, amax_m, amax_v, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_scaled_v_pass2(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                                 const msamp_meta* vmeta, const uint32_t* amax_m,
+                                 const uint32_t* amax_v, const StepConsts& k, hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  const unsigned g = grid_of(nchunks);
+  if (gfmt == kE4M3)
+    k_scaled_v_pass2<kE4M3><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, vmeta, amax_m, amax_v, k);
+  else
+    k_scaled_v_pass2<kE5M2><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, vmeta, amax_m, amax_v, k);
+  return hipGetLastError();
+}
+
 hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* meta,
                                    hipStream_t stream) {
   if (n <= 0) return hipSuccess;
@@ -692,10 +836,11 @@ hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64
 }
 
 hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
-                                uint32_t* amax_b, msamp_meta* meta_b, hipStream_t stream) {
+                                uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
+                                hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   k_step_finalize<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(n, amax_a, meta_a,
-                                                                               amax_b, meta_b);
+                                                                               amax_b, meta_b, fmax_b);
   return hipGetLastError();
 }
 

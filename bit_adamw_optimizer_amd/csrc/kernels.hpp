@@ -65,6 +65,16 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream);
+// Ablation with a per-tensor-scaled FP16 second moment (O2 AdamW): pass 1
+// also reduces amax(v1) into amax_v; pass 2 stores fp16(v1 * s_v).
+hipError_t launch_scaled_v_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                                 const msamp_meta* vmeta, uint32_t* amax_m, uint32_t* amax_v,
+                                 const StepConsts& k, hipStream_t stream);
+hipError_t launch_scaled_v_pass2(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                                 const msamp_meta* vmeta, const uint32_t* amax_m,
+                                 const uint32_t* amax_v, const StepConsts& k, hipStream_t stream);
 hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
@@ -82,9 +92,11 @@ hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* me
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
                            const uint32_t* amax_w, hipStream_t stream);
 // meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then
-// amax_a[t] <- 0; the same for (amax_b, meta_b) when meta_b is not NULL.
+// amax_a[t] <- 0; the same for (amax_b, meta_b) when meta_b is not NULL,
+// with the range fmax_b (448 for an E4M3 copy, 65504 for a scaled FP16 v).
 hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
-                                uint32_t* amax_b, msamp_meta* meta_b, hipStream_t stream);
+                                uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
+                                hipStream_t stream);
 hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipStream_t stream);
 
 }  // namespace msamp

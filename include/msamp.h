@@ -244,6 +244,23 @@ msamp_status msamp_adamw_o2_step_delayed(int32_t n, const int64_t* numel, const 
                                          uint16_t* const* exp_avg_sq, uint16_t* const* weight,
                                          const msamp_adamw_hparams* hp, int64_t step, void* stream);
 
+/*
+ * msamp_adamw_o2_step_scaled_v -- ABLATION, not the step defined above: the
+ * O2 AdamW step with a per-tensor-scaled FP16 second moment, which keeps v
+ * from underflowing binary16 at small gradient scales. exp_avg_sq holds
+ * fp16(v * s_v) and exp_avg_sq_meta[t] = {amax_v, s_v, 1/s_v, 0} with
+ * s_v = scale(amax(v), 65504) (initial meta {0, 1, 1, 0}); v0 is decoded as
+ * f32(code) * exp_avg_sq_meta.scale_inv. Pass 1 also reads v and reduces
+ * amax(v1): 15 bytes per element. Other arguments, layouts and errors as
+ * msamp_adamw_o2_step.
+ */
+msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, msamp_meta* exp_avg_sq_meta,
+                                          uint16_t* const* weight, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream);
+
 /* Frees every cached device table of the library (all devices) after
  * waiting for the devices to finish. Safe to call at any time from one
  * thread while no other library call runs. */

@@ -79,11 +79,13 @@ def u32(a) -> np.ndarray:
 class GpuState:
     """Device state of one workload, driven through the C ABI."""
 
-    def __init__(self, w: W.Workload, device, adam: bool = False, delayed: bool = False):
+    def __init__(self, w: W.Workload, device, adam: bool = False, delayed: bool = False,
+                 scaled_v: bool = False):
         self.w = w
         self.device = device
         self.adam = adam  # Adam (coupled L2) instead of AdamW
         self.delayed = delayed  # one-pass delayed-scaling ablation (O2 AdamW)
+        self.scaled_v = scaled_v  # scaled-FP16-v ablation (O2 AdamW)
         self.weights = W.init_weights(w, device)  # FP16 weight (O2) or master (O3)
         st = M.allocate_state(self.weights, w.level)
         self.exp_avg = st["exp_avg"]
@@ -91,6 +93,7 @@ class GpuState:
         self.exp_avg_sq = st["exp_avg_sq"]
         self.weight_fp8 = st.get("weight_fp8")
         self.weight_fp8_meta = st.get("weight_fp8_meta")
+        self.exp_avg_sq_meta = M.new_meta(w.n, device) if scaled_v else None
         self.grad_q = [torch.empty(k, dtype=torch.uint8, device=device) for k in w.numel]
         self.grad_meta = M.new_meta(w.n, device)
         self.grad_f32 = [torch.empty(k, dtype=torch.float32, device=device) for k in w.numel]
@@ -110,7 +113,11 @@ class GpuState:
         w = self.w
         M.amax(self.tl_g32, self.grad_meta)
         M.quantize_fp8(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq)
-        if w.level == "O2" and self.delayed:
+        if w.level == "O2" and self.scaled_v:
+            M.adamw_o2_step_scaled_v(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m,
+                                     self.exp_avg_meta, self.tl_v, self.exp_avg_sq_meta, self.tl_w,
+                                     step=step, **w.hparams())
+        elif w.level == "O2" and self.delayed:
             M.adamw_o2_step_delayed(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m,
                                     self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
         elif w.level == "O2":
@@ -131,16 +138,17 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda",
-               adam: bool = False, delayed: bool = False):
+               adam: bool = False, delayed: bool = False, scaled_v: bool = False):
     """Runs 'steps' steps on the GPU and on the oracle (for the tensors in
     'verify', default all) and returns a dict of Stats per output. adam=True
     runs the Adam (coupled L2) entry points instead of AdamW."""
     verify = list(range(w.n)) if verify is None else list(verify)
     t0 = time.time()
-    gs = GpuState(w, device, adam=adam, delayed=delayed)
+    gs = GpuState(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v)
     torch.cuda.synchronize()
-    ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam, delayed=delayed) for t in verify}
-    stats = {k: Stats() for k in ("m", "v", "w", "w8", "m_meta", "w8_meta")}
+    ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam, delayed=delayed,
+                            scaled_v=scaled_v) for t in verify}
+    stats = {k: Stats() for k in ("m", "v", "w", "w8", "m_meta", "v_meta", "w8_meta")}
     pool = ThreadPoolExecutor(max_workers=threads)
     hp = w.hparams()
     for s in range(1, steps + 1):
@@ -156,6 +164,7 @@ def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device
         gmeta = gs.grad_meta.cpu().numpy()
         mmeta = gs.exp_avg_meta.cpu().numpy()
         w8meta = gs.weight_fp8_meta.cpu().numpy() if w.level == "O3" else None
+        vmeta = gs.exp_avg_sq_meta.cpu().numpy() if scaled_v else None
         for t in verify:
             qg, gm = refs[t]
             # gradient codes and meta: bit-exact (identical binary32 inputs)
@@ -174,6 +183,8 @@ def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device
             stats["v"].add(host(gs.exp_avg_sq[t]), o.v, "f16", where)
             stats["w"].add(host(gs.weights[t]), o.w, "f16", where)
             stats["m_meta"].add(u32(mmeta[t, :3]), u32(o.m_meta[:3]), "f32", where)
+            if scaled_v:
+                stats["v_meta"].add(u32(vmeta[t, :3]), u32(o.v_meta[:3]), "f32", where)
             if w.level == "O3":
                 stats["w8"].add(host(gs.weight_fp8[t]), o.w8, "fp8", where)
                 stats["w8_meta"].add(u32(w8meta[t, :3]), u32(o.w8_meta[:3]), "f32", where)

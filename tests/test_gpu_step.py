@@ -95,6 +95,32 @@ def test_delayed_scaling_ablation_10_steps():
     assert_bar(stats)
 
 
+def test_scaled_v_ablation_10_steps():
+    """O2 AdamW with a per-tensor-scaled FP16 second moment (an ablation
+    entry point): parity with the oracle's ablation, including the v meta;
+    at gradient scale 1e-3 its v stays representable where the literal FP16
+    v of the O2 step underflows to zero."""
+    w = W.make("single_1m")
+    stats, gs, _ = run_parity(w, 10, scaled_v=True)
+    _report("scaled_v single_1m", stats)
+    assert_bar(stats)
+    v_scaled = host(gs.exp_avg_sq[0])
+    _, gp, _ = run_parity(w, 1)
+    v_plain = host(gp.exp_avg_sq[0])
+    assert (v_scaled != 0).mean() > 0.99
+    assert (v_plain != 0).mean() < 0.01
+    sizes = [0, 1, 15, 17, 4097, 65537, 131072 + 4096 + 9]
+    wr = W.Workload("scaled_v_ragged", "O2", W.E5M2, 4, ["t%d" % i for i in range(len(sizes))],
+                    sizes, grad_kind="student_t3", lr=5e-3, betas=(0.8, 0.99), eps=1e-7,
+                    weight_decay=0.2, seed_base=15)
+    stats, _, _ = run_parity(wr, 4, scaled_v=True)
+    _report(wr.name, stats)
+    assert_bar(stats)
+    stats, _, _ = run_parity(W.make("tiny_llama"), 10, scaled_v=True)
+    _report("scaled_v tiny_llama", stats)
+    assert_bar(stats)
+
+
 def test_ragged_sizes_o2_and_o3():
     """Sizes around the 16-element vector, the 4096-element tile and the
     65536-element chunk, including empty tensors."""
