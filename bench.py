@@ -257,16 +257,16 @@ def summarize_profiles(dirs, workload: str) -> None:
         vals = [v for k, vs in agg.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs]
         return max(vals)  # the one big calibration copy
 
+    # each profiled run keeps its own output (the bench line) in <dir>/bench.log
     def source_hash(d):
-        for f in glob.glob(os.path.join(os.path.dirname(d.rstrip("/")), "*.log")) + \
-                glob.glob(os.path.join(os.path.dirname(d.rstrip("/")), "*.json")):
+        for f in glob.glob(os.path.join(d, "*.log")):
             for line in open(f, errors="replace"):
                 if line.startswith("{") and "kernel_source_hash" in line:
                     return json.loads(line)["kernel_source_hash"]
         return None
 
     copy_bytes = None
-    for f in glob.glob(os.path.join(os.path.dirname(cfetch_dir.rstrip("/")), "*.log")):
+    for f in glob.glob(os.path.join(cfetch_dir, "*.log")):
         for line in open(f, errors="replace"):
             if line.startswith("{") and "calibrate_copy_bytes_read" in line:
                 copy_bytes = json.loads(line)["calibrate_copy_bytes_read"]
@@ -276,6 +276,7 @@ def summarize_profiles(dirs, workload: str) -> None:
     fetch = counters(fetch_dir, "FETCH_SIZE")
     write = counters(write_dir, "WRITE_SIZE")
     h = source_hash(fetch_dir)
+    assert h is not None and h == source_hash(write_dir), "counter runs of different kernel sources"
 
     from bit_adamw_optimizer_amd import workloads as W
     w = W.make(workload)
@@ -283,13 +284,16 @@ def summarize_profiles(dirs, workload: str) -> None:
     lines = ["# HBM traffic per launch, %s (%d params), from rocprofv3 counters" % (workload, w.params), "",
              "Commands (run from the repository root; R=$PWD; cd /tmp first):",
              "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_fetch -o fetch -- python3 $R/bench.py "
-             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile" % workload,
+             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
+             "> $R/gpurun_out/pmc_fetch/bench.log 2>&1" % workload,
              "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_write -o write -- python3 $R/bench.py "
-             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile" % workload,
+             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
+             "> $R/gpurun_out/pmc_write/bench.log 2>&1" % workload,
              "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_copy_fetch -o cfetch -- python3 "
-             "$R/bench.py --calibrate-copy 4",
+             "$R/bench.py --calibrate-copy 4 > $R/gpurun_out/pmc_copy_fetch/bench.log 2>&1",
              "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_copy_write -o cwrite -- python3 "
-             "$R/bench.py --calibrate-copy 4",
+             "$R/bench.py --calibrate-copy 4 > $R/gpurun_out/pmc_copy_write/bench.log 2>&1",
+             "  (each run's directory is made first with mkdir -p)",
              "  python bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/pmc_fetch "
              "gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write --workload %s" % workload,
              "",
@@ -322,7 +326,9 @@ def summarize_profiles(dirs, workload: str) -> None:
         tl = ["# rocprofv3 kernel-trace statistics, %s (%d params)" % (workload, w.params), "",
               "Command (run from the repository root; R=$PWD; cd /tmp first):",
               "  rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o o2_7b -- python3 "
-              "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline" % workload, "",
+              "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline "
+              "> $R/gpurun_out/prof_trace/bench.log 2>&1" % workload, "",
+              "Kernel sources hash: %s" % source_hash(trace_dir), "",
               "| kernel | calls | average ms | min ms | max ms | algorithmic GB/s (avg) |", "|---|---|---|---|---|---|"]
         for r in rows:
             if "msamp::" not in r["Name"]:
