@@ -220,7 +220,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     if (k > INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "tensor too large for the chunk map");
     total += k;
   }
-  if (total > (int64_t)UINT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks");
+  if (total > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks for one launch");
   chunks.reserve((size_t)total);
   for (int32_t t = 0; t < n; ++t) {
     int64_t k = (numel[t] + kChunk - 1) / kChunk;

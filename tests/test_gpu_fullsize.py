@@ -75,3 +75,64 @@ def test_stress_e5m2_10_steps():
         assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
     del gs
     torch.cuda.empty_cache()
+
+
+def test_one_tensor_beyond_2_pow_32_elements():
+    """One tensor of 2^32 + 4099 elements (FP8 byte offsets past 2^32, FP16
+    past 2^33, a ragged last chunk): gradient amax and quantize and two O2
+    steps through the C ABI, checked against the oracle on windows at the
+    start, around element 2^31, below 2^32 and at the end (across 2^32).
+    Each step plants the largest |gradient| at one index inside the windows,
+    always positive. The windows then hold the tensor's gradient amax, and,
+    since the rounded update is monotone in |m0| and |g| for equal signs, its
+    first-moment amax too: the oracle run on the concatenated windows sees
+    the whole tensor's scales, and every other output is element-wise."""
+    import bit_adamw_optimizer_amd as M
+    import oracle as O
+    from tests.parity import Stats, u32
+
+    dev = "cuda"
+    n = (1 << 32) + 4099
+    plant = (1 << 32) + 5
+    wins = [(0, 70_000), ((1 << 31) - 70_000, (1 << 31) + 70_000),
+            ((1 << 32) - 200_000, (1 << 32) - 100_000), (n - 90_000, n)]
+    assert all(a < b <= c for (a, b), (c, _) in zip(wins, wins[1:]))
+    assert wins[3][0] <= plant < wins[3][1]
+    idx = torch.cat([torch.arange(a, b, device=dev) for a, b in wins])
+    log("one tensor of %d elements; checking %d of them" % (n, idx.numel()))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    w = torch.empty(n, dtype=torch.float16, device=dev)
+    step_elems = 1 << 30
+    for a in range(0, n, step_elems):
+        b = min(n, a + step_elems)
+        w[a:b] = (torch.randn(b - a, generator=gen, device=dev) * 0.02).to(torch.float16)
+    m = torch.zeros(n, dtype=torch.uint8, device=dev)
+    v = torch.zeros(n, dtype=torch.float16, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    x = torch.empty(n, dtype=torch.float32, device=dev)
+    gmeta, mmeta = M.new_meta(1, dev), M.new_meta(1, dev)
+    hp = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    torch.cuda.synchronize()
+    ost = O.TensorState(w[idx].cpu().numpy().view(np.uint16), "O2")
+    stats = {k: Stats() for k in ("m", "v", "w")}
+    for s in (1, 2):
+        x.uniform_(-1e-3, 1e-3, generator=gen)
+        x[plant] = 0.02
+        M.amax([x], gmeta)
+        M.quantize_fp8([x], O.E4M3, gmeta, [q])
+        M.adamw_o2_step([q], O.E4M3, gmeta, [m], mmeta, [v], [w], step=s, **hp)
+        torch.cuda.synchronize()
+        qg, gm = O.step_tensor(ost, x[idx].cpu().numpy(), O.E4M3, s, **hp)
+        assert np.array_equal(u32(gmeta[0, :3].cpu().numpy()), u32(gm[:3])), (gmeta, gm)
+        assert np.array_equal(q[idx].cpu().numpy(), qg)
+        where = "step %d" % s
+        stats["m"].add(m[idx].cpu().numpy(), ost.m, "fp8", where)
+        stats["v"].add(v[idx].cpu().numpy().view(np.uint16), ost.v, "f16", where)
+        stats["w"].add(w[idx].cpu().numpy().view(np.uint16), ost.w, "f16", where)
+        assert np.array_equal(u32(mmeta[0, :3].cpu().numpy()), u32(ost.m_meta[:3]))
+        assert int(m[plant]) == 0x7E
+        _report("2^32+ step %d" % s, stats)
+    assert_bar(stats)
+    del x, q, m, v, w
+    torch.cuda.empty_cache()
