@@ -42,9 +42,11 @@ PASS3_BYTES = 2 + 1          # read master FP16, write FP8 copy
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device code's sources (kernels and codec; not the host
+    ABI layer), to tell whether stored counter profiles still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_adamw_optimizer_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ("codec.hpp", "kernels.hpp", "kernels.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -236,6 +238,9 @@ def summarize_profiles(dirs, workload: str) -> None:
 
     trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
 
+    def rel(d):
+        return os.path.relpath(os.path.abspath(d), ROOT)
+
     def one(pattern):
         files = glob.glob(os.path.join(pattern, "**", "*.csv"), recursive=True)
         return files
@@ -283,19 +288,19 @@ def summarize_profiles(dirs, workload: str) -> None:
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     lines = ["# HBM traffic per launch, %s (%d params), from rocprofv3 counters" % (workload, w.params), "",
              "Commands (run from the repository root; R=$PWD; cd /tmp first):",
-             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_fetch -o fetch -- python3 $R/bench.py "
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o fetch -- python3 $R/bench.py "
              "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
-             "> $R/gpurun_out/pmc_fetch/bench.log 2>&1" % workload,
-             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_write -o write -- python3 $R/bench.py "
+             "> $R/%s/bench.log 2>&1" % (rel(fetch_dir), workload, rel(fetch_dir)),
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o write -- python3 $R/bench.py "
              "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
-             "> $R/gpurun_out/pmc_write/bench.log 2>&1" % workload,
-             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_copy_fetch -o cfetch -- python3 "
-             "$R/bench.py --calibrate-copy 4 > $R/gpurun_out/pmc_copy_fetch/bench.log 2>&1",
-             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_copy_write -o cwrite -- python3 "
-             "$R/bench.py --calibrate-copy 4 > $R/gpurun_out/pmc_copy_write/bench.log 2>&1",
+             "> $R/%s/bench.log 2>&1" % (rel(write_dir), workload, rel(write_dir)),
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o cfetch -- python3 "
+             "$R/bench.py --calibrate-copy 4 > $R/%s/bench.log 2>&1" % (rel(cfetch_dir), rel(cfetch_dir)),
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o cwrite -- python3 "
+             "$R/bench.py --calibrate-copy 4 > $R/%s/bench.log 2>&1" % (rel(cwrite_dir), rel(cwrite_dir)),
              "  (each run's directory is made first with mkdir -p)",
-             "  python bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/pmc_fetch "
-             "gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write --workload %s" % workload,
+             "  python bench.py --summarize-profiles %s --workload %s"
+             % (" ".join(rel(d) for d in dirs), workload),
              "",
              "Calibration: a %d-byte device copy reads FETCH_SIZE x %.4f and WRITE_SIZE x %.4f bytes;"
              " these factors scale the counters below." % (copy_bytes, ffac, wfac),
@@ -325,9 +330,11 @@ def summarize_profiles(dirs, workload: str) -> None:
     if rows:
         tl = ["# rocprofv3 kernel-trace statistics, %s (%d params)" % (workload, w.params), "",
               "Command (run from the repository root; R=$PWD; cd /tmp first):",
-              "  rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof_trace -o o2_7b -- python3 "
+              "  rocprofv3 --kernel-trace --stats -f csv -d $R/%s -o %s -- python3 "
               "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline "
-              "> $R/gpurun_out/prof_trace/bench.log 2>&1" % workload, "",
+              "> $R/%s/bench.log 2>&1"
+              % (rel(trace_dir), os.path.basename(stats[0])[:-len("_kernel_stats.csv")], workload,
+                 rel(trace_dir)), "",
               "Kernel sources hash: %s" % source_hash(trace_dir), "",
               "| kernel | calls | average ms | min ms | max ms | algorithmic GB/s (avg) |", "|---|---|---|---|---|---|"]
         for r in rows:
