@@ -116,7 +116,7 @@ const char* msamp_last_error(void);
 
 /*
  * msamp_amax -- per-tensor amax of binary32 tensors ([OL] per-tensor scaled
- * FP8 gradients; [TE] "a pass through memory").
+ * FP8 gradients; [TE]: a format cast costs one full pass over the tensor).
  *   x[t]      device float[numel[t]]
  *   meta[t]   device; .amax is written, the other fields are left unchanged
  * Reads 4 bytes per element.
