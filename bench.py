@@ -373,7 +373,7 @@ def main() -> int:
         summarize_profiles(args.summarize_profiles, args.workload)
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
     import torch

@@ -22,7 +22,7 @@ def _has_gpu() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are never silently skipped on a GPU machine: if a gpu-marked test
+    # GPU tests are never silently skipped on a host with a GPU: if a gpu-marked test
     # is selected and no GPU is visible, it fails loudly inside the test via
     # the binding. On a CPU-only host they are skipped unless explicitly
     # requested with -m gpu.
