@@ -182,9 +182,12 @@ void evict_locked(PlanCache& c) {
 // Returns the plan of a tensor list, building and uploading it (on 'stream')
 // the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n);
 // 'min_one_chunk' gives every tensor at least one (possibly empty) chunk.
+// On success '*lease' holds the cache lock: the caller keeps it until its
+// launches are enqueued, so that no other thread can evict (and free) the
+// plan in between.
 msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
                       const void* const* const* ptrs, int nroles, bool min_one_chunk,
-                      hipStream_t stream, Plan** out) {
+                      hipStream_t stream, Plan** out, std::unique_lock<std::mutex>* lease) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -200,13 +203,14 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   const uint64_t h = hash_words(key);
 
   PlanCache& c = cache();
-  std::lock_guard<std::mutex> lk(c.mu);
+  std::unique_lock<std::mutex> lk(c.mu);
   auto it = c.map.find(h);
   if (it != c.map.end()) {
     for (auto& p : it->second)
       if (p->key == key) {
         p->last_use = ++c.tick;
         *out = p.get();
+        *lease = std::move(lk);
         return MSAMP_OK;
       }
   }
@@ -284,6 +288,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   c.map[h].push_back(std::move(plan));
   // Never evict the plan just returned: it is the most recently used.
   evict_locked(c);
+  *lease = std::move(lk);
   return MSAMP_OK;
 }
 
@@ -399,7 +404,8 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
                                  (const void* const*)exp_avg_sq, (const void* const*)weight,
                                  (const void* const*)weight_fp8};
   Plan* p = nullptr;
-  MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p));
+  std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+  MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, coupled);
 
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
@@ -439,7 +445,8 @@ msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* 
   const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p));
+  std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_scaled_v_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -474,7 +481,8 @@ msamp_status step_delayed_impl(int32_t n, const int64_t* numel, const uint8_t* c
   const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p));
+  std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_O2_DELAYED, s,
                launch_step_delayed(grad_fmt, false, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -534,7 +542,8 @@ msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel, 
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[1] = {(const void* const*)x};
     Plan* p = nullptr;
-    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, false, s, &p));
+    std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, false, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_AMAX, s, launch_amax(p->desc, p->chunks, p->nchunks, p->scratch_a, s));
     MSAMP_LAUNCH(MSAMP_KERNEL_AMAX_FINALIZE, s, launch_amax_finalize(n, p->scratch_a, meta, s));
     return MSAMP_OK;
@@ -556,7 +565,8 @@ static msamp_status quantize_impl(int32_t n, const float* const* x, const int64_
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[2] = {(const void* const*)x, (const void* const*)q};
     Plan* p = nullptr;
-    MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, 2, true, s, &p));
+    std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+    MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, 2, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE, s,
                  launch_quantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, world, s));
     return MSAMP_OK;
@@ -589,7 +599,8 @@ msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int6
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[2] = {(const void* const*)q, (const void* const*)out};
     Plan* p = nullptr;
-    MSAMP_TRY(get_plan(kPlanDequantize, n, numel, roles, 2, false, s, &p));
+    std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+    MSAMP_TRY(get_plan(kPlanDequantize, n, numel, roles, 2, false, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_DEQUANTIZE, s,
                  launch_dequantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, s));
     return MSAMP_OK;

@@ -12,7 +12,8 @@
  *         optimizers are torch.optim.Adam and torch.optim.AdamW; "Features":
  *         memory-limited operations read one byte per element.
  *   [TE]  TransformerEngine issue #131, "FP8 questions": the two FP8 formats
- *         E4M3 and E5M2; a cast between precisions is a pass through memory.
+ *         E4M3 and E5M2; converting a tensor between precisions costs a
+ *         full read and write of it.
  * The arithmetic the pages leave open is fixed as follows (identical in every
  * entry point):
  *   - FP8 formats are the OCP encodings: E4M3 (max 448, no Inf, NaN =
@@ -57,6 +58,9 @@
  *     the pointer lists; msamp_release_cache() frees them.
  *   - Calls that use the same tensor lists must be ordered (same stream, or
  *     synchronized): they share that list's amax scratch.
+ *   - Entry points may be called from several host threads at once; they
+ *     take an internal lock while they look up the cached tables and enqueue
+ *     their kernels, so a table is never freed under a call that uses it.
  *   - Errors: every argument is validated before anything is enqueued; on an
  *     error nothing is enqueued and a status other than MSAMP_OK is returned,
  *     with a description from msamp_last_error() (per thread). No C++

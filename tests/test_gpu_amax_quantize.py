@@ -161,3 +161,43 @@ def test_prescaled_quantize_matches_oracle(fmt):
             assert np.array_equal(u32(m[0, :3].cpu().numpy()), u32(mr[:3]))
     with pytest.raises(M.MsampError):
         M.quantize_fp8_prescaled(dx[0], fmt, metas[0], 0, q[:1])
+
+
+def test_concurrent_threads_with_plan_eviction():
+    """Four host threads, each with 24 tensor lists of its own (96 lists in
+    all, more than the plan cache keeps), call amax and quantize in turn, so
+    that plans are evicted while other threads are launching. Every result is
+    checked against the oracle bit for bit."""
+    import threading
+
+    log("threads + plan eviction")
+    rng = np.random.default_rng(55)
+    lists = [[_tensors(rng, [int(k)], specials=False)[0] for k in rng.integers(1, 9000, 3)]
+             for _ in range(96)]
+    dev_lists = [_to_dev(xs) for xs in lists]
+    errors = []
+
+    def worker(tid):
+        try:
+            for rep in range(3):
+                for j in range(tid, 96, 4):
+                    xs, dx = lists[j], dev_lists[j]
+                    meta = M.new_meta(len(xs), DEV)
+                    q = [torch.empty(x.size, dtype=torch.uint8, device=DEV) for x in xs]
+                    M.amax(dx, meta)
+                    M.quantize_fp8(dx, O.E4M3, meta, q)
+                    torch.cuda.current_stream().synchronize()
+                    mg = meta.cpu().numpy()
+                    for t, x in enumerate(xs):
+                        qr, mr = O.quantize_fp8(x, O.E4M3)
+                        assert np.array_equal(u32(mg[t, :3]), u32(mr[:3])), (tid, j, t)
+                        assert np.array_equal(q[t].cpu().numpy(), qr), (tid, j, t)
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:3]
