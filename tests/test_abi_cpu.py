@@ -147,3 +147,25 @@ def test_grad_generators_are_seeded():
     assert torch.equal(a, b) and not torch.equal(a, c)
     z = next(iter(w.zero_tensors))
     assert (W.grad_tensor(w, z, 1, "cpu") == 0).all()
+
+
+def test_header_is_plain_c_and_cxx_and_a_c_program_links(tmp_path):
+    """include/msamp.h compiles as C11 and as C++17, and a C program using
+    only the header links against the library and gets validation errors
+    back without a GPU."""
+    import subprocess
+
+    inc = os.path.join(ROOT, "include")
+    src = os.path.join(ROOT, "tests", "c_abi_smoke.c")
+    hdr_cpp = tmp_path / "h.cpp"
+    hdr_cpp.write_text('#include "msamp.h"\nint main() { return msamp_abi_version() != MSAMP_ABI_VERSION; }\n')
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-I", inc, str(hdr_cpp)],
+                   check=True)
+    libdir = os.path.dirname(M.library_path())
+    exe = tmp_path / "c_abi_smoke"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc, src,
+                    "-o", str(exe), "-L", libdir, "-lmsamp", "-Wl,-rpath," + libdir,
+                    "-Wl,-rpath-link,/opt/rocm/lib"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert "c abi ok" in r.stdout

@@ -123,12 +123,13 @@ def test_scaled_v_ablation_10_steps():
 
 def test_ragged_sizes_o2_and_o3():
     """Sizes around the 16-element vector, the 4096-element tile and the
-    65536-element chunk, including empty tensors."""
+    65536-element chunk, including empty tensors; O3 with both gradient
+    formats."""
     sizes = [0, 1, 7, 15, 16, 17, 31, 4095, 4096, 4097, 65535, 65536, 65537, 131072 + 4096 + 9, 0, 3]
-    for level in ("O2", "O3"):
-        w = W.Workload("ragged_" + level, level, W.E4M3, 4, ["t%d" % i for i in range(len(sizes))],
+    for level, fmt in (("O2", W.E4M3), ("O3", W.E4M3), ("O3", W.E5M2)):
+        w = W.Workload("ragged_%s_%d" % (level, fmt), level, fmt, 4, ["t%d" % i for i in range(len(sizes))],
                        sizes, lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.05, seed_base=11)
-        log("ragged %s" % level)
+        log("ragged %s fmt %d" % (level, fmt))
         stats, gs, _ = run_parity(w, 4)
         _report(w.name, stats)
         assert_bar(stats)
