@@ -472,3 +472,46 @@ def test_optimizer_state_saving_is_62_5_percent():
     assert state_bytes == O.STATE_BYTES_FP8_FP16 == 3
     saving = 1 - state_bytes / O.STATE_BYTES_FP32_FP32
     assert saving == 0.625
+
+
+def _mean_update(kind, sigma, n=4096, steps=1200, tail=400, seed=0):
+    """Mean |w_{t} - w_{t-1}| over the last 'tail' of 'steps' AdamW steps
+    (wd = 0) on N(0, sigma) gradients: the literal O2 state, the scaled-v
+    ablation, or binary32 states."""
+    rng = np.random.default_rng(seed)
+    hp = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0)
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float16).view(np.uint16)
+    if kind == "f32":
+        w = O.f16_decode(w0).astype(np.float32)
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+    else:
+        st = O.TensorState(w0.copy(), "O2", scaled_v=(kind == "scaled_v"))
+    total = 0.0
+    for t in range(1, steps + 1):
+        g = (rng.standard_normal(n) * sigma).astype(np.float32)
+        before = (w if kind == "f32" else O.f16_decode(st.w)).astype(np.float64)
+        if kind == "f32":
+            O.adamw_f32_tensor(g, m, v, w, t, **hp)
+            after = w.astype(np.float64)
+        else:
+            O.step_tensor(st, g, O.E4M3, t, **hp)
+            after = O.f16_decode(st.w).astype(np.float64)
+        if t > steps - tail:
+            total += np.abs(after - before).mean()
+    return total / tail
+
+
+def test_literal_fp16_v_oversizes_updates_at_small_gradient_scale():
+    """Consequence of keeping the second moment as unscaled FP16: at gradient
+    scale 1e-3, (1-b2)*g^2 underflows, v holds no history, the denominator is
+    about sqrt(1-b2)*|g| and the O2 update is many times binary32 AdamW's
+    once the bias correction has faded. At gradient scale 1e-2 the literal
+    layout tracks binary32 AdamW, and the scaled-v ablation tracks it at
+    both scales (same seeds, so all three see the same gradients)."""
+    ref_small = _mean_update("f32", 1e-3)
+    assert _mean_update("o2", 1e-3) > 20 * ref_small
+    assert abs(_mean_update("scaled_v", 1e-3) / ref_small - 1) < 0.05
+    ref = _mean_update("f32", 1e-2)
+    assert abs(_mean_update("o2", 1e-2) / ref - 1) < 0.05
+    assert abs(_mean_update("scaled_v", 1e-2) / ref - 1) < 0.05
