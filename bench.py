@@ -242,6 +242,16 @@ def summarize_profiles(dirs, workload: str) -> None:
     def rel(d):
         return os.path.relpath(os.path.abspath(d), ROOT)
 
+    # the profiled program's arguments, as rocprofv3 echoed them into the
+    # run's own log
+    def bench_args(d):
+        for f in glob.glob(os.path.join(d, "*.log")):
+            for line in open(f, errors="replace"):
+                m = re.search(r"\[rocprofv3\] 'python3 \S*bench\.py([^']*)'", line)
+                if m:
+                    return m.group(1)
+        raise AssertionError("no rocprofv3 command line in %s" % d)
+
     def one(pattern):
         files = glob.glob(os.path.join(pattern, "**", "*.csv"), recursive=True)
         return files
@@ -289,16 +299,14 @@ def summarize_profiles(dirs, workload: str) -> None:
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     lines = ["# HBM traffic per launch, %s (%d params), from rocprofv3 counters" % (workload, w.params), "",
              "Commands (run from the repository root; R=$PWD; cd /tmp first):",
-             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o fetch -- python3 $R/bench.py "
-             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
-             "> $R/%s/bench.log 2>&1" % (rel(fetch_dir), workload, rel(fetch_dir)),
-             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o write -- python3 $R/bench.py "
-             "--workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-profile "
-             "> $R/%s/bench.log 2>&1" % (rel(write_dir), workload, rel(write_dir)),
-             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o cfetch -- python3 "
-             "$R/bench.py --calibrate-copy 4 > $R/%s/bench.log 2>&1" % (rel(cfetch_dir), rel(cfetch_dir)),
-             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o cwrite -- python3 "
-             "$R/bench.py --calibrate-copy 4 > $R/%s/bench.log 2>&1" % (rel(cwrite_dir), rel(cwrite_dir)),
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o fetch -- python3 $R/bench.py%s "
+             "> $R/%s/bench.log 2>&1" % (rel(fetch_dir), bench_args(fetch_dir), rel(fetch_dir)),
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o write -- python3 $R/bench.py%s "
+             "> $R/%s/bench.log 2>&1" % (rel(write_dir), bench_args(write_dir), rel(write_dir)),
+             "  rocprofv3 --pmc FETCH_SIZE -f csv -d $R/%s -o cfetch -- python3 $R/bench.py%s "
+             "> $R/%s/bench.log 2>&1" % (rel(cfetch_dir), bench_args(cfetch_dir), rel(cfetch_dir)),
+             "  rocprofv3 --pmc WRITE_SIZE -f csv -d $R/%s -o cwrite -- python3 $R/bench.py%s "
+             "> $R/%s/bench.log 2>&1" % (rel(cwrite_dir), bench_args(cwrite_dir), rel(cwrite_dir)),
              "  (each run's directory is made first with mkdir -p)",
              "  python bench.py --summarize-profiles %s --workload %s"
              % (" ".join(rel(d) for d in dirs), workload),
@@ -331,11 +339,10 @@ def summarize_profiles(dirs, workload: str) -> None:
     if rows:
         tl = ["# rocprofv3 kernel-trace statistics, %s (%d params)" % (workload, w.params), "",
               "Command (run from the repository root; R=$PWD; cd /tmp first):",
-              "  rocprofv3 --kernel-trace --stats -f csv -d $R/%s -o %s -- python3 "
-              "$R/bench.py --workload %s --steps 5 --warmup 2 --no-cpu-baseline "
+              "  rocprofv3 --kernel-trace --stats -f csv -d $R/%s -o %s -- python3 $R/bench.py%s "
               "> $R/%s/bench.log 2>&1"
-              % (rel(trace_dir), os.path.basename(stats[0])[:-len("_kernel_stats.csv")], workload,
-                 rel(trace_dir)), "",
+              % (rel(trace_dir), os.path.basename(stats[0])[:-len("_kernel_stats.csv")],
+                 bench_args(trace_dir), rel(trace_dir)), "",
               "Kernel sources hash: %s" % source_hash(trace_dir), "",
               "| kernel | calls | average ms | min ms | max ms | algorithmic GB/s (avg) |", "|---|---|---|---|---|---|"]
         for r in rows:
