@@ -43,12 +43,17 @@ PASS3_BYTES = 2 + 1          # read master FP16, write FP8 copy
 
 def kernel_source_hash() -> str:
     """Hash of the device code's sources (kernels and codec; not the host
-    ABI layer), to tell whether stored counter profiles still apply."""
+    ABI layer) with comments and whitespace removed, to tell whether stored
+    counter profiles still apply to the code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_adamw_optimizer_amd", "csrc")
     for name in ("codec.hpp", "kernels.hpp", "kernels.hip"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

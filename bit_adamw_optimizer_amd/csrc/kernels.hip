@@ -13,6 +13,8 @@
 //     512 + l*8 (one 8-byte FP8 access or one 16-byte FP16 access per group)
 //   FP32 streams: lane l owns the 4-element groups at k*256 + l*4, k = 0..3
 //     (one 16-byte access per group)
+//   AdamW pass 1 (FP8 streams only): lane l owns the 16 codes at l*16 (one
+//     16-byte access per stream)
 // A ragged end of a tensor is handled element by element. The work is bound
 // by HBM bandwidth; no matrix cores are involved.
 //
