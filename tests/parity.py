@@ -80,13 +80,16 @@ class GpuState:
     """Device state of one workload, driven through the C ABI."""
 
     def __init__(self, w: W.Workload, device, adam: bool = False, delayed: bool = False,
-                 scaled_v: bool = False):
+                 scaled_v: bool = False, flat: bool = False):
         self.w = w
         self.device = device
         self.adam = adam  # Adam (coupled L2) instead of AdamW
         self.delayed = delayed  # one-pass delayed-scaling ablation (O2 AdamW)
         self.scaled_v = scaled_v  # scaled-FP16-v ablation (O2 AdamW)
-        self.weights = W.init_weights(w, device)  # FP16 weight (O2) or master (O3)
+        # FP16 weight (O2) or master (O3); flat=True puts every role in one
+        # allocation, as the benchmark does
+        out = M.flat_views(w.numel, torch.float16, device) if flat else None
+        self.weights = W.init_weights(w, device, out=out)
         st = M.allocate_state(self.weights, w.level)
         self.exp_avg = st["exp_avg"]
         self.exp_avg_meta = st["exp_avg_meta"]
@@ -94,9 +97,13 @@ class GpuState:
         self.weight_fp8 = st.get("weight_fp8")
         self.weight_fp8_meta = st.get("weight_fp8_meta")
         self.exp_avg_sq_meta = M.new_meta(w.n, device) if scaled_v else None
-        self.grad_q = [torch.empty(k, dtype=torch.uint8, device=device) for k in w.numel]
+        if flat:
+            self.grad_q = M.flat_views(w.numel, torch.uint8, device)
+            self.grad_f32 = M.flat_views(w.numel, torch.float32, device)
+        else:
+            self.grad_q = [torch.empty(k, dtype=torch.uint8, device=device) for k in w.numel]
+            self.grad_f32 = [torch.empty(k, dtype=torch.float32, device=device) for k in w.numel]
         self.grad_meta = M.new_meta(w.n, device)
-        self.grad_f32 = [torch.empty(k, dtype=torch.float32, device=device) for k in w.numel]
         # marshalled once, as an optimizer would
         self.tl_g32 = M.TensorList(self.grad_f32, "f32", "grad_f32")
         self.tl_gq = M.TensorList(self.grad_q, "u8", "grad_q")
@@ -138,13 +145,14 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda",
-               adam: bool = False, delayed: bool = False, scaled_v: bool = False):
+               adam: bool = False, delayed: bool = False, scaled_v: bool = False,
+               flat: bool = False):
     """Runs 'steps' steps on the GPU and on the oracle (for the tensors in
     'verify', default all) and returns a dict of Stats per output. adam=True
     runs the Adam (coupled L2) entry points instead of AdamW."""
     verify = list(range(w.n)) if verify is None else list(verify)
     t0 = time.time()
-    gs = GpuState(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v)
+    gs = GpuState(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, flat=flat)
     torch.cuda.synchronize()
     ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam, delayed=delayed,
                             scaled_v=scaled_v) for t in verify}

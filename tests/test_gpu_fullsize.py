@@ -1,5 +1,6 @@
 """Full-size parameter lists through the same launch path the benchmark
-times (one multi-tensor launch per pass over the whole list), checked
+times (one multi-tensor launch per pass over the whole list, every role in
+one flat allocation as in the benchmark), checked
 against the oracle on a subset of whole tensors. Tensors are independent
 (per-tensor scaling, element-wise update), so a verified tensor is checked
 exactly, whatever else shares the launch. Layouts: MS-AMP "Optimization
@@ -37,7 +38,7 @@ def test_llama2_7b_o2_5_steps():
                       "layers.31.post_attention_layernorm", "norm"])
     log("llama2_7b O2: %d tensors, %d params; verifying %d tensors (%d params)"
         % (w.n, w.params, len(verify), sum(w.numel[t] for t in verify)))
-    stats, gs, _ = run_parity(w, 5, verify=verify)
+    stats, gs, _ = run_parity(w, 5, verify=verify, flat=True)
     _report("llama2_7b", stats)
     assert_bar(stats)
     _code_invariant(gs, w, verify)
@@ -50,7 +51,7 @@ def test_llama2_13b_o3_3_steps():
     verify = _idx(w, ["layers.0.k_proj", "layers.39.input_layernorm", "norm"])
     log("llama2_13b O3: %d tensors, %d params; verifying %d tensors (%d params)"
         % (w.n, w.params, len(verify), sum(w.numel[t] for t in verify)))
-    stats, gs, _ = run_parity(w, 3, verify=verify)
+    stats, gs, _ = run_parity(w, 3, verify=verify, flat=True)
     _report("llama2_13b", stats)
     assert_bar(stats)
     _code_invariant(gs, w, verify)
@@ -67,7 +68,7 @@ def test_stress_e5m2_10_steps():
     small = [t for t in range(w.n) if w.numel[t] <= 8192]
     log("stress O2 E5M2: %d tensors, %d params; verifying the %d small tensors"
         % (w.n, w.params, len(small)))
-    stats, gs, _ = run_parity(w, 10, verify=small)
+    stats, gs, _ = run_parity(w, 10, verify=small, flat=True)
     _report("stress", stats)
     assert_bar(stats)
     mm = gs.exp_avg_meta.cpu().numpy()
