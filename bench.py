@@ -227,6 +227,8 @@ def _kind_of(name: str):
         return ("o3_pass2" if len(targs) > 1 and targs[1] == "true" else "o2_pass2"), PASS2_BYTES
     if fn == "k_o3_pass3":
         return "o3_pass3", PASS3_BYTES
+    if fn == "k_rmw_probe":
+        return "rmw_probe", PASS2_BYTES
     if fn == "k_scaled_v_pass1":  # also reads the FP16 second moment
         return "step_pass1", PASS1_BYTES + 2
     if fn == "k_scaled_v_pass2":
@@ -436,6 +438,18 @@ def main() -> int:
             if n:
                 kernels[k] = {"launches": n, "avg_ms": ms / n}
 
+    # the update pass's traffic without its arithmetic, on the same buffers:
+    # the ceiling the memory system gives the dominant kernel here
+    probe_ms = None
+    if not args.no_profile:
+        M.profile_enable(True)
+        for _ in range(5):
+            M.rmw_probe(st.grad_q, st.tl_m, st.tl_v, st.tl_w)
+        torch.cuda.synchronize()
+        M.profile_enable(False)
+        n_p, ms_p = M.profile_read("rmw_probe")
+        probe_ms = ms_p / n_p if n_p else None
+
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     P = w.params
     # Adam's pass 1 also reads the FP16 weight for its L2 term
@@ -462,6 +476,12 @@ def main() -> int:
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic_from_profiles(dom, w.name, P),
                     "algorithmic_bytes_per_launch": per_kernel_bytes[dom] * P}
+        if probe_ms:
+            ceiling = PASS2_BYTES * P / (probe_ms * 1e-3) / 1e9
+            roofline["same_buffers_ceiling"] = {
+                "GB/s": round(ceiling, 1), "frac": round(achieved / ceiling, 4),
+                "probe": "msamp_rmw_probe: the update pass's loads and stores (read 6, write 5 B/p) "
+                         "without arithmetic, on the same buffers, %.4f ms" % probe_ms}
     opt_ms = sum(kernels[k]["avg_ms"] for k in ("step_pass1", dom, "o3_pass3", "finalize")
                  if k in kernels)
     result = {

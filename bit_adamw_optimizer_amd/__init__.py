@@ -48,7 +48,7 @@ PROBE_F16_TO_F32 = 5
 
 # kernel kinds of msamp_profile_read, in enum order
 KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
-           "o3_pass3", "finalize", "amax_finalize", "o2_delayed"]
+           "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
@@ -114,6 +114,8 @@ def lib():
         L.msamp_adamw_o2_step_scaled_v.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                                    ctypes.POINTER(_HParams), i64, vp]
         L.msamp_adamw_o2_step_scaled_v.restype = st
+        L.msamp_rmw_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp]
+        L.msamp_rmw_probe.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -347,6 +349,21 @@ def adamw_o2_step_scaled_v(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta
         m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs,
         _meta_ptr(exp_avg_sq_meta, g.n, g.device, "exp_avg_sq_meta"), w.ptrs,
         ctypes.byref(hp), int(step), _stream(g.device)))
+
+
+def rmw_probe(grad, exp_avg, exp_avg_sq, weight) -> None:
+    """Measurement aid: the update pass's memory traffic on these tensor
+    lists with none of its arithmetic (m, v, w are rewritten unchanged; see
+    msamp_rmw_probe in include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    _check(lib().msamp_rmw_probe(g.n, g.numel, g.ptrs, m.ptrs, v.ptrs, w.ptrs, _stream(g.device)))
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:

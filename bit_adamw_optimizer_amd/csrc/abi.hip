@@ -527,6 +527,7 @@ const char* msamp_kernel_name(msamp_kernel_kind kind) {
     case MSAMP_KERNEL_FINALIZE: return "finalize";
     case MSAMP_KERNEL_AMAX_FINALIZE: return "amax_finalize";
     case MSAMP_KERNEL_O2_DELAYED: return "o2_delayed";
+    case MSAMP_KERNEL_RMW_PROBE: return "rmw_probe";
     default: return "";
   }
 }
@@ -692,6 +693,28 @@ msamp_status msamp_release_cache(void) {
     c.count = 0;
     c.bytes = 0;
     if (cur >= 0) (void)hipSetDevice(cur);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                             uint8_t* const* exp_avg, uint16_t* const* exp_avg_sq,
+                             uint16_t* const* weight, void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_common(n, numel));
+    if (n == 0) return MSAMP_OK;
+    MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
+    hipStream_t s = (hipStream_t)stream;
+    const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
+                                   (const void* const*)exp_avg_sq, (const void* const*)weight};
+    Plan* p = nullptr;
+    std::unique_lock<std::mutex> lease;  // held until the launch is enqueued
+    MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
+    MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s));
     return MSAMP_OK;
   });
 }

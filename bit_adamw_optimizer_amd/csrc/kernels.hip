@@ -646,6 +646,47 @@ __global__ __launch_bounds__(kBlock) void k_delayed_finalize(int32_t n, uint32_t
 
 // --------------------------------------------------------- codec probe ---
 
+// The memory traffic of the update pass without its arithmetic: read g, m,
+// v, w and write m, v, w back unchanged (the empty asm keeps the compiler
+// from treating the stores of just-loaded values as removable). It measures
+// what the memory system gives this traffic on the very same buffers.
+__global__ __launch_bounds__(kBlock) void k_rmw_probe(const TensorDesc* __restrict__ desc,
+                                                      const ChunkRef* __restrict__ chunks) {
+  const ChunkRange r = chunk_range(chunks, desc);
+  const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
+  GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
+  GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    const int64_t e0 = group8_base(tile), e1 = e0 + 512;
+    if (e1 + 8 <= r.end) {
+      u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
+      u32x2 M0 = load<u32x2>(mq + e0), M1 = load<u32x2>(mq + e1);
+      u32x4 V0 = load<u32x4>(vh + e0), V1 = load<u32x4>(vh + e1);
+      u32x4 W0 = load<u32x4>(wh + e0), W1 = load<u32x4>(wh + e1);
+      asm volatile("" : "+v"(M0), "+v"(M1), "+v"(V0), "+v"(V1), "+v"(W0), "+v"(W1)
+                   : "v"(G0), "v"(G1));
+      store<u32x2>(mq + e0, M0);
+      store<u32x2>(mq + e1, M1);
+      store<u32x4>(vh + e0, V0);
+      store<u32x4>(vh + e1, V1);
+      store<u32x4>(wh + e0, W0);
+      store<u32x4>(wh + e1, W1);
+    } else {
+      for (int h = 0; h < 2; ++h) {
+        const int64_t e = h ? e1 : e0;
+        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
+          uint32_t g = gq[i], m = mq[i], v = vh[i], w = wh[i];
+          asm volatile("" : "+v"(m), "+v"(v), "+v"(w) : "v"(g));
+          mq[i] = (uint8_t)m;
+          vh[i] = (uint16_t)v;
+          wh[i] = (uint16_t)w;
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void k_codec_probe(int op, const void* __restrict__ in,
                                                         void* __restrict__ out, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
@@ -851,6 +892,13 @@ hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipS
   int64_t blocks = (n + kBlock - 1) / kBlock;
   if (blocks > 65536) blocks = 65536;
   k_codec_probe<<<(unsigned)blocks, kBlock, 0, stream>>>(op, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmw_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
+                            hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  k_rmw_probe<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
   return hipGetLastError();
 }
 

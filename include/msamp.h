@@ -294,6 +294,20 @@ typedef enum {
 msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int64_t n,
                                void* stream);
 
+/*
+ * msamp_rmw_probe -- MEASUREMENT AID, not part of the method: reads g, m, v
+ * and w of an O2 step's tensor lists (or g, m, v and the master of an O3
+ * list) and writes m, v and w back UNCHANGED, with the lanes, tiles and
+ * launch shape of the update pass but none of its arithmetic: 6 bytes read
+ * and 5 written per element. Its rate on the caller's own buffers is the
+ * ceiling the memory system gives the update pass's traffic there. Arguments
+ * as msamp_adamw_o2_step; the same work must not run concurrently on these
+ * tensors.
+ */
+msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                             uint8_t* const* exp_avg, uint16_t* const* exp_avg_sq,
+                             uint16_t* const* weight, void* stream);
+
 /* Kernel timing with HIP events recorded on the launch stream around every
  * kernel the library enqueues (off by default). */
 typedef enum {
@@ -307,7 +321,8 @@ typedef enum {
   MSAMP_KERNEL_FINALIZE = 7,    /* per-tensor meta write-back of a step */
   MSAMP_KERNEL_AMAX_FINALIZE = 8, /* amax write-back of msamp_amax */
   MSAMP_KERNEL_O2_DELAYED = 9,  /* one-pass delayed-scaling ablation */
-  MSAMP_KERNEL_COUNT = 10
+  MSAMP_KERNEL_RMW_PROBE = 10,  /* msamp_rmw_probe (measurement aid) */
+  MSAMP_KERNEL_COUNT = 11
 } msamp_kernel_kind;
 
 /* on != 0 starts recording (and discards earlier records); on == 0 stops. */

@@ -215,3 +215,19 @@ def test_step_argument_errors():
     assert e.value.status == 2
     torch.cuda.synchronize()
     assert torch.equal(before, gs.weights[0])
+
+
+def test_rmw_probe_leaves_every_stream_unchanged():
+    """msamp_rmw_probe (measurement aid) rewrites m, v and w with their own
+    values and never writes g, on ragged sizes and both tails."""
+    sizes = [0, 1, 15, 17, 4097, 65537, 131072 + 4096 + 9]
+    g = [torch.randint(0, 256, (k,), dtype=torch.uint8, device="cuda") for k in sizes]
+    m = [torch.randint(0, 256, (k,), dtype=torch.uint8, device="cuda") for k in sizes]
+    v = [torch.randint(0, 1 << 15, (k,), dtype=torch.int16, device="cuda").view(torch.float16) for k in sizes]
+    w = [torch.randint(0, 1 << 15, (k,), dtype=torch.int16, device="cuda").view(torch.float16) for k in sizes]
+    before = [t.clone() for t in g + m + v + w]
+    for _ in range(3):
+        M.rmw_probe(g, m, v, w)
+    torch.cuda.synchronize()
+    after = g + m + v + w
+    assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(after, before))
