@@ -195,14 +195,31 @@ def cpu_baseline(w, device, threads: int) -> dict:
     grads = [W.grad_tensor(sub, t, 1, device).cpu().numpy() for t in range(sub.n)]
     states = [O.TensorState(x, w.level) for x in weights]
     nthreads = max(1, min(threads, len(idx)))
+    # one thread on the first tensor of the sample (fresh state, same inputs)
+    one = O.TensorState(weights[0].copy(), w.level)
+    t0 = time.perf_counter()
+    O.step_list([one], grads[:1], w.grad_fmt, 1, threads=1, **w.hparams())
+    dt1 = time.perf_counter() - t0
     t0 = time.perf_counter()
     O.step_list(states, grads, w.grad_fmt, 1, threads=nthreads, **w.hparams())
     dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": sub.params / dt, "unit": "params/s", "cores": nthreads, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": "%d tensors (%s), %d params, one step (grad amax + quantize + %s step), "
                       "one oracle thread per tensor" % (sub.n, ", ".join(sub.names[:3]) + ", ...",
-                                                         sub.params, w.level)}
+                                                         sub.params, w.level),
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "one_thread": {"value": sub.numel[0] / dt1, "unit": "params/s",
+                           "sample": "%s (%d params)" % (sub.names[0], sub.numel[0])},
+            "full_step_seconds_extrapolated": round(w.params / (sub.params / dt), 2)}
 
 
 def _kind_of(name: str):
@@ -522,6 +539,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, device, args.cpu_threads)
+        result["cpu_baseline"]["gpu_over_oracle"] = round(result["value"] / result["cpu_baseline"]["value"], 1)
     print(json.dumps(result), flush=True)
     return 0
 
