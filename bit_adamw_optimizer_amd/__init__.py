@@ -69,6 +69,10 @@ class _HParams(ctypes.Structure):
                 ("weight_decay", ctypes.c_double)]
 
 
+class _StepConstants(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("b1", "ob1", "b2", "ob2", "eps", "ss", "ibs", "dec", "wd")]
+
+
 _lib = None
 
 
@@ -116,6 +120,15 @@ def lib():
         L.msamp_adamw_o2_step_scaled_v.restype = st
         L.msamp_rmw_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp]
         L.msamp_rmw_probe.restype = st
+        L.msamp_step_constants_compute.argtypes = [ctypes.POINTER(_HParams), i64, ctypes.c_int,
+                                                   ctypes.POINTER(_StepConstants)]
+        L.msamp_step_constants_compute.restype = st
+        L.msamp_adamw_o2_step_devconst.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.c_int, vp]
+        L.msamp_adamw_o2_step_devconst.restype = st
+        L.msamp_adamw_o3_step_devconst.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                   vp, vp, ctypes.c_int, vp]
+        L.msamp_adamw_o3_step_devconst.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -310,6 +323,67 @@ def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
         m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
         w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
         ctypes.byref(hp), int(step), _stream(g.device)))
+
+
+def step_constants(*, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int,
+                   adam: bool = False) -> torch.Tensor:
+    """The binary32 constants of one AdamW (adam=True: Adam) step as a CPU
+    float32 tensor of 9 values (msamp_step_constants), bit-identical to what
+    the by-value step entry points use."""
+    out = _StepConstants()
+    hp = _hp(lr, betas, eps, weight_decay)
+    _check(lib().msamp_step_constants_compute(ctypes.byref(hp), int(step), int(bool(adam)),
+                                              ctypes.byref(out)))
+    return torch.tensor([getattr(out, k) for k, _ in _StepConstants._fields_], dtype=torch.float32)
+
+
+def _consts_ptr(consts: torch.Tensor, device):
+    if not isinstance(consts, torch.Tensor) or consts.dtype != torch.float32 or consts.numel() != 9 \
+            or not consts.is_contiguous():
+        raise ValueError("consts must be a contiguous float32 tensor of 9 values")
+    if consts.device != device:
+        raise ValueError("consts is not on %s" % device)
+    return ctypes.c_void_p(consts.data_ptr())
+
+
+def adamw_o2_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                           consts: torch.Tensor, *, adam: bool = False) -> None:
+    """The O2 step with its constants read from the device tensor 'consts'
+    when the kernels run (capturable in a HIP graph; see
+    msamp_adamw_o2_step_devconst in include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    _check(lib().msamp_adamw_o2_step_devconst(
+        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+        _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
+
+
+def adamw_o3_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, master,
+                           weight_fp8, weight_fp8_meta, consts: torch.Tensor, *,
+                           adam: bool = False) -> None:
+    """The O3 step with its constants read from the device tensor 'consts'
+    (see msamp_adamw_o3_step_devconst in include/msamp.h)."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(master, "f16", "master")
+    w8 = _tl(weight_fp8, "u8", "weight_fp8")
+    for other, name in ((m, "exp_avg"), (v, "exp_avg_sq"), (w, "master"), (w8, "weight_fp8")):
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    _check(lib().msamp_adamw_o3_step_devconst(
+        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+        w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
+        _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
 
 
 def adam_o2_step(*args, **kw) -> None:

@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -383,12 +384,16 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
                        msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
                        uint16_t* const* weight, uint8_t* const* weight_fp8,
                        msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp, int64_t step,
-                       void* stream_ptr) {
+                       void* stream_ptr, const StepConsts* kdev = nullptr) {
   g_last_error.clear();
   MSAMP_TRY(check_common(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
-  MSAMP_TRY(check_hparams(hp, step));
+  if (kdev == nullptr) {
+    MSAMP_TRY(check_hparams(hp, step));
+  } else if (((uintptr_t)kdev & 3u) != 0) {
+    return fail(MSAMP_E_MISALIGNED, "consts is not 4-byte aligned");
+  }
   MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
   MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
   MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
@@ -406,14 +411,14 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
   MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p, &lease));
-  const StepConsts k = make_consts(hp, step, coupled);
+  const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
 
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, k, s));
+                                 exp_avg_meta, p->scratch_a, k, s, kdev));
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s));
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
                  launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
@@ -651,6 +656,51 @@ msamp_status msamp_adam_o3_step(int32_t n, const int64_t* numel, const uint8_t* 
   return guarded([&]() {
     return step_impl(true, true, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                      exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, stream);
+  });
+}
+
+static_assert(sizeof(msamp_step_constants) == sizeof(StepConsts), "constants layout");
+static_assert(offsetof(msamp_step_constants, ibs) == offsetof(StepConsts, ibs), "constants layout");
+static_assert(offsetof(msamp_step_constants, wd) == offsetof(StepConsts, wd), "constants layout");
+
+msamp_status msamp_step_constants_compute(const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                          msamp_step_constants* out) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_hparams(hp, step));
+    if (out == nullptr) return fail(MSAMP_E_INVALID_ARG, "out is NULL");
+    const StepConsts k = make_consts(hp, step, coupled != 0);
+    std::memcpy(out, &k, sizeof k);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_adamw_o2_step_devconst(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                          const msamp_step_constants* consts, int coupled,
+                                          void* stream) {
+  return guarded([&]() -> msamp_status {
+    if (consts == nullptr) return fail(MSAMP_E_INVALID_ARG, "consts is NULL");
+    return step_impl(false, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                     exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, nullptr, 0, stream,
+                     (const StepConsts*)consts);
+  });
+}
+
+msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                          uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                          const msamp_step_constants* consts, int coupled,
+                                          void* stream) {
+  return guarded([&]() -> msamp_status {
+    if (consts == nullptr) return fail(MSAMP_E_INVALID_ARG, "consts is NULL");
+    return step_impl(true, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                     exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, nullptr, 0, stream,
+                     (const StepConsts*)consts);
   });
 }
 

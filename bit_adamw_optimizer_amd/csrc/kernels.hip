@@ -295,14 +295,18 @@ __device__ __forceinline__ void second_moment_and_weight(const StepConsts& k, fl
 }
 
 // Pass 1 (O2 and O3): new first moment and its per-tensor amax. Adam
-// (COUPLED) also reads the weight for its L2 term.
+// (COUPLED) also reads the weight for its L2 term. The step constants come
+// by value (kv), or from device memory when kdev is not null (so that a
+// captured launch can be replayed for later steps).
 template <int GF, bool COUPLED>
 __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
                                                        const msamp_meta* __restrict__ mmeta,
                                                        uint32_t* __restrict__ amax_m,
-                                                       StepConsts k) {
+                                                       StepConsts kv,
+                                                       const StepConsts* __restrict__ kdev) {
+  const StepConsts k = kdev != nullptr ? *kdev : kv;
   const ChunkRange r = chunk_range(chunks, desc);
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
@@ -370,8 +374,10 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
                                                        const msamp_meta* __restrict__ mmeta,
                                                        const uint32_t* __restrict__ amax_m,
                                                        uint32_t* __restrict__ amax_w,
-                                                       StepConsts k) {
+                                                       StepConsts kv,
+                                                       const StepConsts* __restrict__ kdev) {
   static_assert(!(O3 && DELAYED), "the delayed-scaling ablation is O2 only");
+  const StepConsts k = kdev != nullptr ? *kdev : kv;
   const ChunkRange r = chunk_range(chunks, desc);
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
@@ -766,21 +772,22 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
 template <int GF, bool COUPLED>
 static void pass1_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
-                         const StepConsts& k) {
-  k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+                         const StepConsts& k, const StepConsts* kdev) {
+  k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
 }
 
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
-                             uint32_t* amax_m, const StepConsts& k, hipStream_t stream) {
+                             uint32_t* amax_m, const StepConsts& k, hipStream_t stream,
+                             const StepConsts* kdev) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3) {
-    if (coupled) pass1_launch<kE4M3, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
-    else pass1_launch<kE4M3, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+    if (coupled) pass1_launch<kE4M3, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else pass1_launch<kE4M3, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
   } else {
-    if (coupled) pass1_launch<kE5M2, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
-    else pass1_launch<kE5M2, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k);
+    if (coupled) pass1_launch<kE5M2, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else pass1_launch<kE5M2, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
   }
   return hipGetLastError();
 }
@@ -788,34 +795,35 @@ hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, con
 template <int GF, bool O3, bool COUPLED>
 static void pass2_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, const uint32_t* amax_m,
-                         uint32_t* amax_w, const StepConsts& k) {
-  k_step_pass2<GF, O3, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+                         uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev) {
+  k_step_pass2<GF, O3, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k,
+                                                          kdev);
 }
 
 template <int GF>
 static void pass2_dispatch(bool o3, bool coupled, unsigned g, hipStream_t stream,
                            const TensorDesc* desc, const ChunkRef* chunks, const msamp_meta* gmeta,
                            const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                           const StepConsts& k) {
+                           const StepConsts& k, const StepConsts* kdev) {
   if (o3) {
-    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
   } else {
-    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
-    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
   }
 }
 
 hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                             const StepConsts& k, hipStream_t stream) {
+                             const StepConsts& k, hipStream_t stream, const StepConsts* kdev) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3)
-    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
   else
-    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k);
+    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
   return hipGetLastError();
 }
 
@@ -826,14 +834,14 @@ hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, c
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3) {
     if (coupled)
-      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
     else
-      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
   } else {
     if (coupled)
-      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
     else
-      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k);
+      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
   }
   return hipGetLastError();
 }

@@ -44,6 +44,8 @@ struct ChunkRef {
 // AdamW / Adam constants of one step (binary64 expressions rounded once).
 // dec is 1 - lr*wd for AdamW and exactly 1 for Adam; wd is the coupled L2
 // coefficient used by Adam only.
+// The step kernels take them by value, or read them from device memory
+// (the graph-capturable entry points); the layout is msamp_step_constants.
 struct StepConsts {
   float b1, ob1, b2, ob2, eps, ss, ibs, dec, wd;
 };
@@ -64,7 +66,8 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
 // moments); otherwise AdamW.
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
-                             uint32_t* amax_m, const StepConsts& k, hipStream_t stream);
+                             uint32_t* amax_m, const StepConsts& k, hipStream_t stream,
+                             const StepConsts* kdev = nullptr);
 // Ablation with a per-tensor-scaled FP16 second moment (O2 AdamW): pass 1
 // also reduces amax(v1) into amax_v; pass 2 stores fp16(v1 * s_v).
 hipError_t launch_scaled_v_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks,
@@ -78,7 +81,8 @@ hipError_t launch_scaled_v_pass2(int gfmt, const TensorDesc* desc, const ChunkRe
 hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                             const StepConsts& k, hipStream_t stream);
+                             const StepConsts& k, hipStream_t stream,
+                             const StepConsts* kdev = nullptr);
 // Ablation: the O2 update in one pass with delayed scaling of the first
 // moment (encode with scale(mmeta.amax) of the previous step; reduce the new
 // amax into amax_new).

@@ -295,6 +295,44 @@ msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int
                                void* stream);
 
 /*
+ * Graph-capturable steps. The per-step constants of the AdamW definition
+ * above (B1 OB1 B2 OB2 EPS SS IBS DEC, plus WD = (float)weight_decay for
+ * Adam's L2 term; DEC is exactly 1 for Adam), in that order. The *_devconst
+ * steps read them from DEVICE memory when their kernels run instead of
+ * taking hparams and step by value, so a captured launch sequence (HIP
+ * graph) can be replayed for later steps after the caller rewrites the
+ * record. Everything else about them is the step of the same layout.
+ */
+typedef struct {
+  float b1, ob1, b2, ob2, eps, ss, ibs, dec, wd;
+} msamp_step_constants;
+
+/* Host only: the constants of step 'step' (>= 1) for AdamW (coupled = 0) or
+ * Adam (coupled = 1), bit-identical to what the by-value steps use. */
+msamp_status msamp_step_constants_compute(const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                          msamp_step_constants* out);
+
+/* msamp_adamw_o2_step / msamp_adam_o2_step (coupled = 0 / 1) with the
+ * constants read from consts (device, 4-byte aligned, one record), which
+ * must hold the record for the step being taken when the kernels run. */
+msamp_status msamp_adamw_o2_step_devconst(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                          const msamp_step_constants* consts, int coupled,
+                                          void* stream);
+
+/* msamp_adamw_o3_step / msamp_adam_o3_step (coupled = 0 / 1) with the
+ * constants read from consts (device), as above. */
+msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                          msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                          uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                          uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                          uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                          const msamp_step_constants* consts, int coupled,
+                                          void* stream);
+
+/*
  * msamp_rmw_probe -- MEASUREMENT AID, not part of the method: reads g, m, v
  * and w of an O2 step's tensor lists (or g, m, v and the master of an O3
  * list) and writes m, v and w back UNCHANGED, with the lanes, tiles and

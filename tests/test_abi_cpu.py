@@ -169,3 +169,24 @@ def test_header_is_plain_c_and_cxx_and_a_c_program_links(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stderr)
     assert "c abi ok" in r.stdout
+
+
+def test_step_constants_match_the_oracle_bit_for_bit():
+    """msamp_step_constants_compute (host only) against the oracle's own
+    binary64-then-binary32 constants, AdamW and Adam, over many steps and
+    hyperparameters."""
+    import numpy as np
+
+    import oracle as O
+
+    for hp in (dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),
+               dict(lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.2)):
+        for step in (1, 2, 3, 10, 100, 1000, 12345, 10**6):
+            for adam in (False, True):
+                got = M.step_constants(step=step, adam=adam, **hp).numpy()
+                ref = np.asarray(O.adamw_constants(step, **hp), np.float32)
+                if adam:
+                    ref[7] = 1.0  # no decoupled decay for Adam
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (hp, step, adam, got, ref)
+    with pytest.raises(M.MsampError):
+        M.step_constants(step=0)

@@ -231,3 +231,54 @@ def test_rmw_probe_leaves_every_stream_unchanged():
     torch.cuda.synchronize()
     after = g + m + v + w
     assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(after, before))
+
+
+@pytest.mark.parametrize("level,adam", [("O2", False), ("O3", True)])
+def test_graph_captured_step_replays_later_steps_bit_exact(level, adam):
+    """amax + quantize + the device-constants step captured once in a HIP
+    graph (torch.cuda.graph) and replayed for steps 2..6, with the step's
+    constants rewritten in device memory and new gradients written between
+    replays (eager work and a synchronization in between every time). After
+    every replay the whole state equals the eager by-value entry points' bit
+    for bit."""
+    w = W.make("tiny_llama_o3" if level == "O3" else "tiny_llama")
+    if adam:
+        w.weight_decay = 0.1
+    log("graph replay %s adam=%s" % (level, adam))
+    ref = GpuState(w, "cuda", adam=adam)
+    gr = GpuState(w, "cuda", adam=adam)
+    consts = torch.empty(9, dtype=torch.float32, device="cuda")
+
+    def graph_step():
+        M.amax(gr.tl_g32, gr.grad_meta)
+        M.quantize_fp8(gr.tl_g32, w.grad_fmt, gr.grad_meta, gr.tl_gq)
+        if level == "O3":
+            M.adamw_o3_step_devconst(gr.tl_gq, w.grad_fmt, gr.grad_meta, gr.tl_m, gr.exp_avg_meta,
+                                     gr.tl_v, gr.tl_w, gr.tl_w8, gr.weight_fp8_meta, consts, adam=adam)
+        else:
+            M.adamw_o2_step_devconst(gr.tl_gq, w.grad_fmt, gr.grad_meta, gr.tl_m, gr.exp_avg_meta,
+                                     gr.tl_v, gr.tl_w, consts, adam=adam)
+
+    def state(gs):
+        ts = gs.exp_avg + gs.exp_avg_sq + gs.weights + gs.grad_q + [gs.exp_avg_meta, gs.grad_meta]
+        if level == "O3":
+            ts += gs.weight_fp8 + [gs.weight_fp8_meta]
+        return [t.view(torch.uint8) if t.dtype == torch.float16 else t for t in ts]
+
+    graph = None
+    for s in range(1, 7):
+        ref.fill_grads(s)
+        ref.step(s)
+        gr.fill_grads(s)
+        consts.copy_(M.step_constants(step=s, adam=adam, **w.hparams()))
+        if s == 1:
+            graph_step()  # eager: builds the cached tables before the capture
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                graph_step()
+        else:
+            graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(state(ref), state(gr)):
+            assert torch.equal(a, b), "step %d differs" % s
