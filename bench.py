@@ -72,6 +72,9 @@ def parse():
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--graph", action="store_true",
+                   help="capture amax + quantize + the device-constants step in a HIP graph per "
+                        "gradient buffer and replay it (AdamW / Adam only)")
     p.add_argument("--no-profile", action="store_true",
                    help="do not bracket kernels with HIP events")
     p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -130,11 +133,59 @@ class State:
             self.grad_sets.append(M.TensorList(g, "f32", "grad_f32"))
         torch.cuda.synchronize()
 
+    def enable_graphs(self, total_steps: int) -> None:
+        """Switch to the device-constants step: the constants of every step
+        are computed up front into a device table; each step copies its row
+        into the record the kernels read and replays the graph captured for
+        its gradient buffer (captured after two eager steps have built the
+        cached tables)."""
+        import torch
+
+        import bit_adamw_optimizer_amd as M
+
+        w = self.w
+        dev = self.exp_avg_meta.device
+        self.consts = torch.empty(9, dtype=torch.float32, device=dev)
+        self.table = torch.stack([M.step_constants(step=t, adam=self.adam, **w.hparams())
+                                  for t in range(1, total_steps + 1)]).to(dev)
+        self.graphs = None
+        self.use_graphs = True
+
+    def _graph_body(self, g32) -> None:
+        import bit_adamw_optimizer_amd as M
+
+        w = self.w
+        M.amax(g32, self.grad_meta)
+        M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
+        if w.level == "O2":
+            M.adamw_o2_step_devconst(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m,
+                                     self.exp_avg_meta, self.tl_v, self.tl_w, self.consts, adam=self.adam)
+        else:
+            M.adamw_o3_step_devconst(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m,
+                                     self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
+                                     self.weight_fp8_meta, self.consts, adam=self.adam)
+
     def step(self, step: int) -> None:
         import bit_adamw_optimizer_amd as M
 
         w = self.w
         g32 = self.grad_sets[(step - 1) % 2]
+        if getattr(self, "use_graphs", False):
+            import torch
+
+            self.consts.copy_(self.table[step - 1])
+            if step <= 2:
+                self._graph_body(g32)  # eager: builds the cached tables of both buffers
+                if step == 2:
+                    self.graphs = []
+                    for gs in self.grad_sets:
+                        gr = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(gr):
+                            self._graph_body(gs)
+                        self.graphs.append(gr)
+            else:
+                self.graphs[(step - 1) % 2].replay()
+            return
         M.amax(g32, self.grad_meta)
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2" and self.scaled_v:
@@ -431,6 +482,14 @@ def main() -> int:
         print("the %s ablation exists for the O2 layout only" % args.optimizer, file=sys.stderr)
         return 2
     st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v)
+    if args.graph:
+        if delayed or scaled_v:
+            print("--graph covers the AdamW and Adam steps only", file=sys.stderr)
+            return 2
+        if args.warmup < 2:
+            print("--graph needs --warmup >= 2 (the graphs are captured at step 2)", file=sys.stderr)
+            return 2
+        st.enable_graphs(args.warmup + args.steps)
 
     step = 0
     for _ in range(args.warmup):
@@ -515,15 +574,17 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s FP8 %s step, %d tensors, %d params, %s grads "
-                               "(amax + quantize + step per iteration)"
+                               "(amax + quantize + step per iteration%s)"
                                % (w.name, w.level, {"adam": "Adam", "adamw": "AdamW",
                                                     "adamw-delayed": "AdamW one-pass delayed-scaling "
                                                                      "ablation",
                                                     "adamw-scaled-v": "AdamW scaled-FP16-v "
                                                                       "ablation"}[args.optimizer],
                                   w.n, P,
-                                  "E4M3" if w.grad_fmt == 0 else "E5M2"),
-                   "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P},
+                                  "E4M3" if w.grad_fmt == 0 else "E5M2",
+                                  ", HIP-graph replay" if args.graph else ""),
+                   "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P,
+                   "graph": bool(args.graph)},
         "hbm_gbps": round(gbps, 1),
         "pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_param": path_bytes,
