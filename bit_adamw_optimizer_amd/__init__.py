@@ -243,8 +243,9 @@ def amax(x, meta: torch.Tensor) -> None:
     x = _tl(x, "f32", "x")
     if x.n == 0:
         return
-    _check(lib().msamp_amax(x.n, x.ptrs, x.numel, _meta_ptr(meta, x.n, x.device, "meta"),
-                            _stream(x.device)))
+    with torch.cuda.device(x.device):
+        _check(lib().msamp_amax(x.n, x.ptrs, x.numel, _meta_ptr(meta, x.n, x.device, "meta"),
+                                _stream(x.device)))
 
 
 def quantize_fp8(x, fmt: int, meta: torch.Tensor, q) -> None:
@@ -255,9 +256,10 @@ def quantize_fp8(x, fmt: int, meta: torch.Tensor, q) -> None:
     x.matches(q, "q")
     if x.n == 0:
         return
-    _check(lib().msamp_quantize_fp8(x.n, x.ptrs, x.numel, int(fmt),
-                                    _meta_ptr(meta, x.n, x.device, "meta"), q.ptrs,
-                                    _stream(x.device)))
+    with torch.cuda.device(x.device):
+        _check(lib().msamp_quantize_fp8(x.n, x.ptrs, x.numel, int(fmt),
+                                        _meta_ptr(meta, x.n, x.device, "meta"), q.ptrs,
+                                        _stream(x.device)))
 
 
 def quantize_fp8_prescaled(x, fmt: int, meta: torch.Tensor, world_size: int, q) -> None:
@@ -268,9 +270,10 @@ def quantize_fp8_prescaled(x, fmt: int, meta: torch.Tensor, world_size: int, q) 
     x.matches(q, "q")
     if x.n == 0:
         return
-    _check(lib().msamp_quantize_fp8_prescaled(x.n, x.ptrs, x.numel, int(fmt),
-                                              _meta_ptr(meta, x.n, x.device, "meta"),
-                                              int(world_size), q.ptrs, _stream(x.device)))
+    with torch.cuda.device(x.device):
+        _check(lib().msamp_quantize_fp8_prescaled(x.n, x.ptrs, x.numel, int(fmt),
+                                                  _meta_ptr(meta, x.n, x.device, "meta"),
+                                                  int(world_size), q.ptrs, _stream(x.device)))
 
 
 def dequantize_fp8(q, fmt: int, meta: torch.Tensor, out) -> None:
@@ -280,9 +283,10 @@ def dequantize_fp8(q, fmt: int, meta: torch.Tensor, out) -> None:
     q.matches(out, "out")
     if q.n == 0:
         return
-    _check(lib().msamp_dequantize_fp8(q.n, q.ptrs, q.numel, int(fmt),
-                                      _meta_ptr(meta, q.n, q.device, "meta"), out.ptrs,
-                                      _stream(q.device)))
+    with torch.cuda.device(q.device):
+        _check(lib().msamp_dequantize_fp8(q.n, q.ptrs, q.numel, int(fmt),
+                                          _meta_ptr(meta, q.n, q.device, "meta"), out.ptrs,
+                                          _stream(q.device)))
 
 
 def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
@@ -298,10 +302,11 @@ def adamw_o2_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
     if g.n == 0:
         return
     hp = _hp(lr, betas, eps, weight_decay)
-    _check(getattr(lib(), _entry)(
-        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
-        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
-        ctypes.byref(hp), int(step), _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(getattr(lib(), _entry)(
+            g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+            m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+            ctypes.byref(hp), int(step), _stream(g.device)))
 
 
 def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, master,
@@ -318,11 +323,12 @@ def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
     if g.n == 0:
         return
     hp = _hp(lr, betas, eps, weight_decay)
-    _check(getattr(lib(), _entry)(
-        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
-        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
-        w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
-        ctypes.byref(hp), int(step), _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(getattr(lib(), _entry)(
+            g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+            m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+            w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
+            ctypes.byref(hp), int(step), _stream(g.device)))
 
 
 def step_constants(*, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int,
@@ -359,10 +365,11 @@ def adamw_o2_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta
         g.matches(other, name)
     if g.n == 0:
         return
-    _check(lib().msamp_adamw_o2_step_devconst(
-        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
-        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
-        _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(lib().msamp_adamw_o2_step_devconst(
+            g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+            m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+            _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
 
 
 def adamw_o3_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, master,
@@ -379,11 +386,12 @@ def adamw_o3_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta
         g.matches(other, name)
     if g.n == 0:
         return
-    _check(lib().msamp_adamw_o3_step_devconst(
-        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
-        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
-        w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
-        _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(lib().msamp_adamw_o3_step_devconst(
+            g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+            m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
+            w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
+            _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
 
 
 def adam_o2_step(*args, **kw) -> None:
@@ -418,11 +426,12 @@ def adamw_o2_step_scaled_v(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta
     if g.n == 0:
         return
     hp = _hp(lr, betas, eps, weight_decay)
-    _check(lib().msamp_adamw_o2_step_scaled_v(
-        g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
-        m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs,
-        _meta_ptr(exp_avg_sq_meta, g.n, g.device, "exp_avg_sq_meta"), w.ptrs,
-        ctypes.byref(hp), int(step), _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(lib().msamp_adamw_o2_step_scaled_v(
+            g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, g.device, "grad_meta"),
+            m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs,
+            _meta_ptr(exp_avg_sq_meta, g.n, g.device, "exp_avg_sq_meta"), w.ptrs,
+            ctypes.byref(hp), int(step), _stream(g.device)))
 
 
 def rmw_probe(grad, exp_avg, exp_avg_sq, weight) -> None:
@@ -437,7 +446,8 @@ def rmw_probe(grad, exp_avg, exp_avg_sq, weight) -> None:
         g.matches(other, name)
     if g.n == 0:
         return
-    _check(lib().msamp_rmw_probe(g.n, g.numel, g.ptrs, m.ptrs, v.ptrs, w.ptrs, _stream(g.device)))
+    with torch.cuda.device(g.device):
+        _check(lib().msamp_rmw_probe(g.n, g.numel, g.ptrs, m.ptrs, v.ptrs, w.ptrs, _stream(g.device)))
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:
@@ -446,9 +456,10 @@ def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:
         raise ValueError("codec_probe needs device tensors")
     if inp.numel() != out.numel() or not inp.is_contiguous() or not out.is_contiguous():
         raise ValueError("codec_probe needs contiguous tensors of equal size")
-    _check(lib().msamp_codec_probe(int(op), ctypes.c_void_p(inp.data_ptr()),
-                                   ctypes.c_void_p(out.data_ptr()), inp.numel(),
-                                   _stream(inp.device)))
+    with torch.cuda.device(inp.device):
+        _check(lib().msamp_codec_probe(int(op), ctypes.c_void_p(inp.data_ptr()),
+                                       ctypes.c_void_p(out.data_ptr()), inp.numel(),
+                                       _stream(inp.device)))
 
 
 def release_cache() -> None:

@@ -52,7 +52,9 @@
  *   - A tensor with numel == 0 may have NULL pointers.
  *   - stream is a hipStream_t (NULL = the null stream). All work is enqueued
  *     on it; nothing synchronizes the host. Inputs must stay alive and
- *     unmodified until that work completes.
+ *     unmodified until that work completes. The calling thread's current HIP
+ *     device must be the device of the tensors and of the stream: the cached
+ *     tables are built on, and looked up for, the current device.
  *   - The caller owns every tensor and meta array. The library owns cached
  *     device tables (tensor descriptors, chunk maps, amax scratch) keyed on
  *     the pointer lists; msamp_release_cache() frees them.
