@@ -134,6 +134,8 @@ def lib():
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
         L.msamp_codec_probe.restype = st
         L.msamp_profile_enable.argtypes = [ctypes.c_int]
+        L.msamp_profile_select.argtypes = [ctypes.c_uint32]
+        L.msamp_profile_select.restype = st
         L.msamp_profile_enable.restype = st
         L.msamp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(i64),
                                          ctypes.POINTER(ctypes.c_double)]
@@ -468,6 +470,12 @@ def release_cache() -> None:
 
 def profile_enable(on: bool) -> None:
     _check(lib().msamp_profile_enable(1 if on else 0))
+
+
+def profile_select(kernels=None) -> None:
+    """Time only these kernel kinds (names from KERNELS; None: all)."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNELS.index(k) for k in kernels)
+    _check(lib().msamp_profile_select(ctypes.c_uint32(mask)))
 
 
 def profile_read(kernel: str):

@@ -42,6 +42,7 @@ msamp_status fail_hip(hipError_t e, const char* what) {
 struct Profiler {
   std::mutex mu;
   bool enabled = false;
+  uint32_t mask = 0xFFFFFFFFu;  // kernel kinds that are timed (bit = kind)
   struct Rec {
     int kind;
     hipEvent_t a, b;
@@ -68,6 +69,9 @@ struct Profiler {
   }
 };
 
+// Events created when timing is switched on (two per timed launch).
+constexpr size_t kProfilerReserve = 4096;
+
 Profiler& profiler() {
   static Profiler* p = new Profiler();  // never destroyed: events may outlive static teardown
   return *p;
@@ -82,7 +86,7 @@ hipError_t timed(msamp_kernel_kind kind, hipStream_t s, F&& launch) {
   bool on;
   {
     std::lock_guard<std::mutex> lk(p.mu);
-    on = p.enabled;
+    on = p.enabled && ((p.mask >> (int)kind) & 1u);
     if (on) {
       a = p.get_event();
       b = p.get_event();
@@ -794,8 +798,24 @@ msamp_status msamp_profile_enable(int on) {
       // discard earlier records; their events must have completed first
       for (auto& r : p.recs) (void)hipEventSynchronize(r.b);
       p.recycle_all();
+      // create the events up front, so that the timed work does not
+      for (size_t i = p.pool.size(); i < kProfilerReserve; ++i) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) break;
+        p.pool.push_back(e);
+      }
     }
     p.enabled = on != 0;
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_profile_select(uint32_t kind_mask) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> lk(p.mu);
+    p.mask = kind_mask;
     return MSAMP_OK;
   });
 }

@@ -365,8 +365,15 @@ typedef enum {
   MSAMP_KERNEL_COUNT = 11
 } msamp_kernel_kind;
 
-/* on != 0 starts recording (and discards earlier records); on == 0 stops. */
+/* on != 0 starts recording (and discards earlier records; the events for
+ * the next 2048 launches are created here, outside the timed work); on == 0
+ * stops. */
 msamp_status msamp_profile_enable(int on);
+
+/* Chooses the kernel kinds that get events (bit k = kind k; default: all).
+ * Each pair of events costs the launch sequence some time, so a caller that
+ * times a whole sequence selects only the kinds it needs. */
+msamp_status msamp_profile_select(uint32_t kind_mask);
 
 /* Waits for the recorded events and returns, for one kernel kind, the number
  * of launches and the summed duration in milliseconds since the last
