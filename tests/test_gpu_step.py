@@ -282,3 +282,45 @@ def test_graph_captured_step_replays_later_steps_bit_exact(level, adam):
         torch.cuda.synchronize()
         for a, b in zip(state(ref), state(gr)):
             assert torch.equal(a, b), "step %d differs" % s
+
+
+@pytest.mark.parametrize("hp", [
+    dict(lr=0.0, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),
+    dict(lr=1e-2, betas=(0.0, 0.999), eps=1e-8, weight_decay=0.01),
+    dict(lr=1e-2, betas=(0.9, 0.0), eps=1e-8, weight_decay=0.01),
+    dict(lr=1e-2, betas=(0.9, 0.999), eps=1.0, weight_decay=0.0),
+], ids=["lr0", "beta1_0", "beta2_0", "eps1"])
+def test_degenerate_hyperparameters(hp):
+    """Limits of the AdamW definition (lr = 0: the weight stays put; beta1 =
+    0; beta2 = 0; eps dominating the denominator), O2 and O3, against the
+    oracle."""
+    sizes = [17, 4097, 65537 + 16]
+    for level in ("O2", "O3"):
+        w = W.Workload("degenerate_" + level, level, W.E4M3, 3, ["t%d" % i for i in range(len(sizes))],
+                       sizes, seed_base=16, **hp)
+        stats, gs, _ = run_parity(w, 3)
+        _report(w.name, stats)
+        assert_bar(stats)
+        if hp["lr"] == 0.0:
+            w0 = W.init_weights(w, "cuda")
+            assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(gs.weights, w0))
+
+
+def test_release_cache_mid_run_is_bit_exact():
+    """Freeing the cached device tables between steps only makes the next
+    call rebuild them: the trajectory is bit-identical to an uninterrupted
+    one."""
+    w = W.make("tiny_llama_o3")
+    a = GpuState(w, "cuda")
+    b = GpuState(w, "cuda")
+    for s in range(1, 5):
+        for gs in (a, b):
+            gs.fill_grads(s)
+            gs.step(s)
+        if s == 2:
+            torch.cuda.synchronize()
+            M.release_cache()
+    torch.cuda.synchronize()
+    for x, y in zip(a.exp_avg + a.exp_avg_sq + a.weights + a.weight_fp8 + [a.exp_avg_meta, a.weight_fp8_meta],
+                    b.exp_avg + b.exp_avg_sq + b.weights + b.weight_fp8 + [b.exp_avg_meta, b.weight_fp8_meta]):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))

@@ -210,6 +210,28 @@ def test_random_tiny_tensors_match_exact_arithmetic(level, gfmt, adam):
     run_both(list(w), grads, gfmt, level, hp, adam)
 
 
+@pytest.mark.parametrize("hp", [
+    dict(lr=0.0, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),   # no update: w1 = w0
+    dict(lr=1e-2, betas=(0.0, 0.999), eps=1e-8, weight_decay=0.01),   # beta1 = 0: m1 = g
+    dict(lr=1e-2, betas=(0.9, 0.0), eps=1e-8, weight_decay=0.01),     # beta2 = 0: v1 = g*g
+    dict(lr=1e-2, betas=(0.9, 0.999), eps=1.0, weight_decay=0.0),     # eps dominates the denominator
+], ids=["lr0", "beta1_0", "beta2_0", "eps1"])
+def test_degenerate_hyperparameters_match_exact_arithmetic(hp):
+    """Limits of the AdamW definition (lr = 0, beta1 = 0, beta2 = 0, large
+    eps) through the same exact-rational evaluation, O2 and O3."""
+    rng = np.random.default_rng(31)
+    n = 6
+    w = O.f16_encode((rng.standard_normal(n) * 0.5).astype(np.float32))
+    grads = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 0, n)).astype(np.float32) for _ in range(3)]
+    for level in ("O2", "O3"):
+        run_both(list(w), grads, O.E4M3, level, hp, False)
+    if hp["lr"] == 0.0:
+        st = O.TensorState(w.copy(), "O2")
+        for t, g in enumerate(grads, 1):
+            O.step_tensor(st, g, O.E4M3, t, **hp)
+        assert np.array_equal(st.w, w)
+
+
 def test_adam_differs_from_adamw_only_through_weight_decay():
     """With wd = 0 Adam and AdamW are the same algorithm; with wd > 0 the
     coupled L2 term changes the moments (and so the stored codes)."""
