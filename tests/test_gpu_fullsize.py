@@ -66,9 +66,12 @@ def test_llama2_13b_o3_3_steps():
 def test_stress_e5m2_10_steps():
     w = W.make("stress")
     small = [t for t in range(w.n) if w.numel[t] <= 8192]
-    log("stress O2 E5M2: %d tensors, %d params; verifying the %d small tensors"
-        % (w.n, w.params, len(small)))
-    stats, gs, _ = run_parity(w, 10, verify=small, flat=True)
+    big = [t for t in range(w.n) if w.numel[t] > 8192]
+    verify = small + [big[0], big[-1]]
+    log("stress O2 E5M2: %d tensors, %d params; verifying the %d small tensors and 2 of the %d "
+        "8192x8192 ones (%d params)" % (w.n, w.params, len(small), len(big),
+                                        sum(w.numel[t] for t in verify)))
+    stats, gs, _ = run_parity(w, 10, verify=verify, flat=True)
     _report("stress", stats)
     assert_bar(stats)
     mm = gs.exp_avg_meta.cpu().numpy()
