@@ -267,35 +267,6 @@ msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const
                                           uint16_t* const* weight, const msamp_adamw_hparams* hp,
                                           int64_t step, void* stream);
 
-/* Frees every cached device table of the library (all devices) after
- * waiting for the devices to finish. Safe to call at any time from one
- * thread while no other library call runs. */
-msamp_status msamp_release_cache(void);
-
-/* ----------------------------------------------------------------------
- * Test- and measurement-facing entry points.
- * ---------------------------------------------------------------------- */
-
-/* Element-wise device codec used by every kernel above, exposed so that it
- * can be compared with an independent codec on every input of interest:
- *   MSAMP_PROBE_F32_TO_E4M3 / _E5M2  in float[n]    -> out uint8[n] (unscaled
- *                                    saturating cast)
- *   MSAMP_PROBE_E4M3_TO_F32 / _E5M2  in uint8[n]    -> out float[n]
- *   MSAMP_PROBE_F32_TO_F16           in float[n]    -> out uint16[n]
- *   MSAMP_PROBE_F16_TO_F32           in uint16[n]   -> out float[n]
- * in/out are device pointers, 16-byte aligned; n >= 0. */
-typedef enum {
-  MSAMP_PROBE_F32_TO_E4M3 = 0,
-  MSAMP_PROBE_F32_TO_E5M2 = 1,
-  MSAMP_PROBE_E4M3_TO_F32 = 2,
-  MSAMP_PROBE_E5M2_TO_F32 = 3,
-  MSAMP_PROBE_F32_TO_F16 = 4,
-  MSAMP_PROBE_F16_TO_F32 = 5
-} msamp_probe_op;
-
-msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int64_t n,
-                               void* stream);
-
 /*
  * Graph-capturable steps. The per-step constants of the AdamW definition
  * above (B1 OB1 B2 OB2 EPS SS IBS DEC, plus WD = (float)weight_decay for
@@ -333,6 +304,35 @@ msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const
                                           uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                           const msamp_step_constants* consts, int coupled,
                                           void* stream);
+
+/* Frees every cached device table of the library (all devices) after
+ * waiting for the devices to finish. Safe to call at any time from one
+ * thread while no other library call runs. */
+msamp_status msamp_release_cache(void);
+
+/* ----------------------------------------------------------------------
+ * Test- and measurement-facing entry points.
+ * ---------------------------------------------------------------------- */
+
+/* Element-wise device codec used by every kernel above, exposed so that it
+ * can be compared with an independent codec on every input of interest:
+ *   MSAMP_PROBE_F32_TO_E4M3 / _E5M2  in float[n]    -> out uint8[n] (unscaled
+ *                                    saturating cast)
+ *   MSAMP_PROBE_E4M3_TO_F32 / _E5M2  in uint8[n]    -> out float[n]
+ *   MSAMP_PROBE_F32_TO_F16           in float[n]    -> out uint16[n]
+ *   MSAMP_PROBE_F16_TO_F32           in uint16[n]   -> out float[n]
+ * in/out are device pointers, 16-byte aligned; n >= 0. */
+typedef enum {
+  MSAMP_PROBE_F32_TO_E4M3 = 0,
+  MSAMP_PROBE_F32_TO_E5M2 = 1,
+  MSAMP_PROBE_E4M3_TO_F32 = 2,
+  MSAMP_PROBE_E5M2_TO_F32 = 3,
+  MSAMP_PROBE_F32_TO_F16 = 4,
+  MSAMP_PROBE_F16_TO_F32 = 5
+} msamp_probe_op;
+
+msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int64_t n,
+                               void* stream);
 
 /*
  * msamp_rmw_probe -- MEASUREMENT AID, not part of the method: reads g, m, v
