@@ -118,6 +118,16 @@ def lib():
         L.msamp_adamw_o2_step_scaled_v.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                                    ctypes.POINTER(_HParams), i64, vp]
         L.msamp_adamw_o2_step_scaled_v.restype = st
+        o2_args = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
+        o3_args = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+        hp_args = [ctypes.POINTER(_HParams), i64, ctypes.c_int]
+        L.msamp_adamw_o2_step_phase1.argtypes = o2_args + hp_args + [vp, vp]
+        L.msamp_adamw_o2_step_phase2.argtypes = o2_args + hp_args + [vp, vp]
+        L.msamp_adamw_o3_step_phase1.argtypes = o3_args + hp_args + [vp, vp]
+        L.msamp_adamw_o3_step_phase2.argtypes = o3_args + hp_args + [vp, vp, vp]
+        L.msamp_adamw_o3_step_phase3.argtypes = o3_args + [vp, vp]
+        for f in ("o2_step_phase1", "o2_step_phase2", "o3_step_phase1", "o3_step_phase2", "o3_step_phase3"):
+            getattr(L, "msamp_adamw_" + f).restype = st
         L.msamp_rmw_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp]
         L.msamp_rmw_probe.restype = st
         L.msamp_step_constants_compute.argtypes = [ctypes.POINTER(_HParams), i64, ctypes.c_int,
@@ -394,6 +404,58 @@ def adamw_o3_step_devconst(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta
             m.ptrs, _meta_ptr(exp_avg_meta, g.n, g.device, "exp_avg_meta"), v.ptrs, w.ptrs,
             w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, g.device, "weight_fp8_meta"),
             _consts_ptr(consts, g.device), int(bool(adam)), _stream(g.device)))
+
+
+def _amax_ptr(a, n: int, device, name: str):
+    if not isinstance(a, torch.Tensor) or a.dtype != torch.float32 or a.numel() != n \
+            or not a.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor of %d values" % (name, n))
+    if n and a.device != device:
+        raise ValueError("%s is not on %s" % (name, device))
+    return ctypes.c_void_p(a.data_ptr() if n else 0)
+
+
+def adamw_step_phase(phase: int, level: str, grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta,
+                     exp_avg_sq, weight, weight_fp8=None, weight_fp8_meta=None, *, amax_in=None,
+                     amax_out=None, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                     step: int = 1, adam: bool = False) -> None:
+    """One phase of the split-phase step on a rank's slices of the tensors
+    (see msamp_adamw_o2_step_phase1 in include/msamp.h). phase 1: amax_out
+    <- local first-moment amax. phase 2: update with the global first-moment
+    amax amax_in (O3: amax_out <- local master amax). phase 3 (O3): FP8 copy
+    with the global master amax amax_in."""
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    lists = [(m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")]
+    w8 = None
+    if level == "O3":
+        w8 = _tl(weight_fp8, "u8", "weight_fp8")
+        lists.append((w8, "weight_fp8"))
+    elif level != "O2" or phase == 3:
+        raise ValueError("level must be O2 (phases 1, 2) or O3 (phases 1-3)")
+    for other, name in lists:
+        g.matches(other, name)
+    if g.n == 0:
+        return
+    dev = g.device
+    args = [g.n, g.numel, g.ptrs, int(grad_fmt), _meta_ptr(grad_meta, g.n, dev, "grad_meta"), m.ptrs,
+            _meta_ptr(exp_avg_meta, g.n, dev, "exp_avg_meta"), v.ptrs, w.ptrs]
+    if level == "O3":
+        args += [w8.ptrs, _meta_ptr(weight_fp8_meta, g.n, dev, "weight_fp8_meta")]
+    hp = _hp(lr, betas, eps, weight_decay)
+    if phase in (1, 2):
+        args += [ctypes.byref(hp), int(step), int(bool(adam))]
+    if phase == 2:
+        args.append(_amax_ptr(amax_in, g.n, dev, "amax_in"))
+    if phase == 1 or (phase == 2 and level == "O3"):
+        args.append(_amax_ptr(amax_out, g.n, dev, "amax_out"))
+    if phase == 3:
+        args.append(_amax_ptr(amax_in, g.n, dev, "amax_in"))
+    entry = "msamp_adamw_%s_step_phase%d" % (level.lower(), phase)
+    with torch.cuda.device(dev):
+        _check(getattr(lib(), entry)(*args, _stream(dev)))
 
 
 def adam_o2_step(*args, **kw) -> None:

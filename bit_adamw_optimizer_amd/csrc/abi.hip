@@ -383,6 +383,43 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
     if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
   } while (0)
 
+// The tensor lists and meta arrays of an O2 (o3 = false) or O3 step.
+msamp_status check_step_lists(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                              const msamp_meta* grad_meta, uint8_t* const* exp_avg,
+                              const msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                              uint16_t* const* weight, uint8_t* const* weight_fp8,
+                              const msamp_meta* weight_fp8_meta) {
+  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, o3 ? "master" : "weight"));
+  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
+  if (o3) {
+    MSAMP_TRY(check_list(n, numel, (const void* const*)weight_fp8, "weight_fp8"));
+    MSAMP_TRY(check_meta(n, weight_fp8_meta, "weight_fp8_meta"));
+  }
+  return MSAMP_OK;
+}
+
+// The cached tables of a step's tensor lists (the same plan for every
+// entry point that takes these lists).
+msamp_status step_plan(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                       uint8_t* const* exp_avg, uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                       uint8_t* const* weight_fp8, hipStream_t s, Plan** p,
+                       std::unique_lock<std::mutex>* lease) {
+  const void* const* roles[5] = {(const void* const*)grad, (const void* const*)exp_avg,
+                                 (const void* const*)exp_avg_sq, (const void* const*)weight,
+                                 (const void* const*)weight_fp8};
+  return get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, p, lease);
+}
+
+msamp_status check_amax_array(int32_t n, const float* a, const char* role) {
+  if (n > 0 && a == nullptr) return fail(MSAMP_E_INVALID_ARG, std::string(role) + " is NULL");
+  if (((uintptr_t)a & 3u) != 0) return fail(MSAMP_E_MISALIGNED, std::string(role) + " is not 4-byte aligned");
+  return MSAMP_OK;
+}
+
 msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, const uint8_t* const* grad,
                        int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
                        msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
@@ -398,23 +435,12 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   } else if (((uintptr_t)kdev & 3u) != 0) {
     return fail(MSAMP_E_MISALIGNED, "consts is not 4-byte aligned");
   }
-  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, o3 ? "master" : "weight"));
-  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
-  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
-  if (o3) {
-    MSAMP_TRY(check_list(n, numel, (const void* const*)weight_fp8, "weight_fp8"));
-    MSAMP_TRY(check_meta(n, weight_fp8_meta, "weight_fp8_meta"));
-  }
+  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
+                             weight, weight_fp8, weight_fp8_meta));
   hipStream_t s = (hipStream_t)stream_ptr;
-  const void* const* roles[5] = {(const void* const*)grad, (const void* const*)exp_avg,
-                                 (const void* const*)exp_avg_sq, (const void* const*)weight,
-                                 (const void* const*)weight_fp8};
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, &p, &lease));
+  MSAMP_TRY(step_plan(o3, n, numel, grad, exp_avg, exp_avg_sq, weight, weight_fp8, s, &p, &lease));
   const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
 
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
@@ -511,6 +537,54 @@ msamp_status guarded(F&& f) {
   } catch (...) {
     return fail(MSAMP_E_INVALID_ARG, "internal error");
   }
+}
+
+// Split-phase step for a flat intra-tensor partition (each rank holds a
+// slice of every tensor): phase 1 exports the local amax of the new first
+// moment; phase 2 takes the ranks' MAX of it (O3: and exports the local
+// amax of the new master); phase 3 (O3) takes the MAX of that.
+msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64_t* numel,
+                        const uint8_t* const* grad, int grad_fmt, const msamp_meta* grad_meta,
+                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                        uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                        const msamp_adamw_hparams* hp, int64_t step, float* amax_out,
+                        const float* amax_in, void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  if (phase != 3) MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
+                             weight, weight_fp8, weight_fp8_meta));
+  if (phase == 1 || (phase == 2 && o3)) MSAMP_TRY(check_amax_array(n, amax_out, "amax output"));
+  if (phase >= 2) MSAMP_TRY(check_amax_array(n, amax_in, "amax input"));
+  hipStream_t s = (hipStream_t)stream_ptr;
+  Plan* p = nullptr;
+  std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+  MSAMP_TRY(step_plan(o3, n, numel, grad, exp_avg, exp_avg_sq, weight, weight_fp8, s, &p, &lease));
+  if (phase == 1) {
+    const StepConsts k = make_consts(hp, step, coupled);
+    MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
+                 launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
+                                   exp_avg_meta, p->scratch_a, k, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_a, amax_out, s));
+  } else if (phase == 2) {
+    const StepConsts k = make_consts(hp, step, coupled);
+    // binary32 amax values are non-negative: their bits order like the
+    // unsigned integers the update pass reads
+    MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
+                 launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
+                                   exp_avg_meta, (const uint32_t*)amax_in, p->scratch_b, k, s));
+    if (o3) MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_b, amax_out, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_meta_from_amax(n, amax_in, exp_avg_meta, 448.0f, s));
+  } else {
+    MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, (const uint32_t*)amax_in, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+                 launch_meta_from_amax(n, amax_in, weight_fp8_meta, 448.0f, s));
+  }
+  return MSAMP_OK;
 }
 
 }  // namespace
@@ -705,6 +779,73 @@ msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const
     return step_impl(true, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
                      exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, nullptr, 0, stream,
                      (const StepConsts*)consts);
+  });
+}
+
+msamp_status msamp_adamw_o2_step_phase1(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        float* amax_m, void* stream) {
+  return guarded([&]() {
+    return phase_impl(1, false, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                      exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, hp, step, amax_m, nullptr,
+                      stream);
+  });
+}
+
+msamp_status msamp_adamw_o2_step_phase2(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        const float* amax_m, void* stream) {
+  return guarded([&]() {
+    return phase_impl(2, false, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                      exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, hp, step, nullptr, amax_m,
+                      stream);
+  });
+}
+
+msamp_status msamp_adamw_o3_step_phase1(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        float* amax_m, void* stream) {
+  return guarded([&]() {
+    return phase_impl(1, true, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                      exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, amax_m,
+                      nullptr, stream);
+  });
+}
+
+msamp_status msamp_adamw_o3_step_phase2(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        const float* amax_m, float* amax_w, void* stream) {
+  return guarded([&]() {
+    return phase_impl(2, true, coupled != 0, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg,
+                      exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step, amax_w,
+                      amax_m, stream);
+  });
+}
+
+msamp_status msamp_adamw_o3_step_phase3(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const float* amax_w, void* stream) {
+  return guarded([&]() {
+    return phase_impl(3, true, false, n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
+                      exp_avg_sq, master, weight_fp8, weight_fp8_meta, nullptr, 0, nullptr, amax_w,
+                      stream);
   });
 }
 

@@ -519,6 +519,33 @@ __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* _
   }
 }
 
+// -------------------------------------------------- split-phase steps ---
+
+// out[t] <- amax[t] (binary32 bits), then amax[t] <- 0: hands a tensor's
+// amax from the scratch to the caller (who combines the ranks' values).
+__global__ __launch_bounds__(kBlock) void k_export_amax(int32_t n, uint32_t* __restrict__ amax,
+                                                        float* __restrict__ out) {
+  const int32_t t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= n) return;
+  out[t] = __uint_as_float(amax[t]);
+  amax[t] = 0u;
+}
+
+// meta[t] <- {a, scale(a, fmax), 1/scale, 0} with a = amax[t] (caller's).
+__global__ __launch_bounds__(kBlock) void k_meta_from_amax(int32_t n, const float* __restrict__ amax,
+                                                           msamp_meta* __restrict__ meta, float fmax) {
+  const int32_t t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= n) return;
+  const float a = amax[t];
+  const float s = scale_rule(a, fmax);
+  msamp_meta m;
+  m.amax = a;
+  m.scale = s;
+  m.scale_inv = 1.0f / s;
+  m.reserved = 0.0f;
+  meta[t] = m;
+}
+
 // ----------------------------------------- scaled-FP16-v ablation (O2) ---
 
 constexpr float kF16Max = 65504.0f;
@@ -900,6 +927,19 @@ hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipS
   int64_t blocks = (n + kBlock - 1) / kBlock;
   if (blocks > 65536) blocks = 65536;
   k_codec_probe<<<(unsigned)blocks, kBlock, 0, stream>>>(op, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_export_amax(int32_t n, uint32_t* amax, float* out, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  k_export_amax<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(n, amax, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_from_amax(int32_t n, const float* amax, msamp_meta* meta, float fmax,
+                                 hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  k_meta_from_amax<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(n, amax, meta, fmax);
   return hipGetLastError();
 }
 

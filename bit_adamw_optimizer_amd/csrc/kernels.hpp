@@ -102,6 +102,11 @@ hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
                                 uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
                                 hipStream_t stream);
 hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipStream_t stream);
+// Split-phase steps: out[t] <- amax[t] as binary32 and amax[t] <- 0; and
+// meta[t] <- {a, scale(a, fmax), 1/scale, 0} from a caller's amax array.
+hipError_t launch_export_amax(int32_t n, uint32_t* amax, float* out, hipStream_t stream);
+hipError_t launch_meta_from_amax(int32_t n, const float* amax, msamp_meta* meta, float fmax,
+                                 hipStream_t stream);
 // Reads g, m, v, w (roles p0..p3) and writes m, v, w back unchanged, with
 // the same lanes, tiles and launch shape as the O2/O3 update pass.
 hipError_t launch_rmw_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,

@@ -305,6 +305,60 @@ msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const
                                           const msamp_step_constants* consts, int coupled,
                                           void* stream);
 
+/*
+ * Split-phase steps, for a flat intra-tensor partition of the parameters
+ * over data-parallel ranks (each rank holds a contiguous slice of every
+ * tensor, as a ZeRO-style sharded optimizer does; [OL] O3: ZeRO and the FP8
+ * weight broadcast). The per-tensor amaxes couple the slices: the caller
+ * combines the ranks' values (an all-reduce MAX over the ranks; binary32
+ * amaxes are non-negative, so MAX on their bits is exact) between phases.
+ * The arguments are those of msamp_adamw_o2_step / msamp_adamw_o3_step for
+ * the rank's slices, with coupled = 0 (AdamW) or 1 (Adam), plus device
+ * float[n] amax arrays (4-byte aligned):
+ *   phase 1  amax_m[t] <- amax of the slice's new first moment; no state
+ *            is written.
+ *   phase 2  the update with s_m = scale(amax_m[t], 448) from the global
+ *            amax_m; exp_avg_meta[t] <- {amax_m, s_m, 1/s_m, 0}. O3 also
+ *            writes amax_w[t] <- amax of the slice's new master.
+ *   phase 3  (O3) the FP8 copy with s_w = scale(amax_w[t], 448) from the
+ *            global amax_w; weight_fp8_meta[t] <- {amax_w, s_w, 1/s_w, 0}.
+ * With the global MAX between the phases, every slice's result is bit-
+ * identical to the slice of the unpartitioned step. Phase 1 and phase 2 of
+ * one step take the same hp and step.
+ */
+msamp_status msamp_adamw_o2_step_phase1(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        float* amax_m, void* stream);
+msamp_status msamp_adamw_o2_step_phase2(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        const float* amax_m, void* stream);
+msamp_status msamp_adamw_o3_step_phase1(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        float* amax_m, void* stream);
+msamp_status msamp_adamw_o3_step_phase2(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const msamp_adamw_hparams* hp, int64_t step, int coupled,
+                                        const float* amax_m, float* amax_w, void* stream);
+msamp_status msamp_adamw_o3_step_phase3(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                        msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                        uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                        uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                        const float* amax_w, void* stream);
+
 /* Frees every cached device table of the library (all devices) after
  * waiting for the devices to finish. Safe to call at any time from one
  * thread while no other library call runs. */

@@ -324,3 +324,75 @@ def test_release_cache_mid_run_is_bit_exact():
     for x, y in zip(a.exp_avg + a.exp_avg_sq + a.weights + a.weight_fp8 + [a.exp_avg_meta, a.weight_fp8_meta],
                     b.exp_avg + b.exp_avg_sq + b.weights + b.weight_fp8 + [b.exp_avg_meta, b.weight_fp8_meta]):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def _slice_bounds(numel, ranks):
+    """Per tensor, the bounds of each rank's contiguous slice (starts rounded
+    up to 16 elements, so that every slice keeps a 16-byte aligned base)."""
+    return [[min(k, -(-(k * r // ranks) // 16) * 16) for r in range(ranks)] + [k] for k in numel]
+
+
+@pytest.mark.parametrize("level,adam", [("O2", False), ("O3", False), ("O3", True)])
+def test_sharded_phases_equal_the_unsharded_step(level, adam):
+    """Three data-parallel ranks emulated on one GPU, each holding a slice of
+    every tensor, run the split-phase step; the per-tensor amaxes are
+    combined with a MAX between the phases (what an all-reduce MAX over the
+    ranks would do). Over 4 steps every byte of the state and every meta
+    record equals the unsharded step's."""
+    ranks = 3
+    w = W.make("tiny_llama_o3" if level == "O3" else "tiny_llama")
+    if adam:
+        w.weight_decay = 0.1
+    hp = w.hparams()
+    log("sharded phases %s adam=%s" % (level, adam))
+    ref = GpuState(w, "cuda", adam=adam)
+    sh = GpuState(w, "cuda", adam=adam)
+    bounds = _slice_bounds(w.numel, ranks)
+
+    def piece(lst, r, kind):
+        return M.TensorList([x[bounds[t][r]:bounds[t][r + 1]] for t, x in enumerate(lst)], kind)
+
+    R = []
+    for r in range(ranks):
+        d = dict(g32=piece(sh.grad_f32, r, "f32"), gq=piece(sh.grad_q, r, "u8"), m=piece(sh.exp_avg, r, "u8"),
+                 v=piece(sh.exp_avg_sq, r, "f16"), w=piece(sh.weights, r, "f16"),
+                 gmeta=M.new_meta(w.n, "cuda"), mmeta=M.new_meta(w.n, "cuda"),
+                 w8=piece(sh.weight_fp8, r, "u8") if level == "O3" else None,
+                 w8meta=M.new_meta(w.n, "cuda") if level == "O3" else None,
+                 amax_m=torch.zeros(w.n, dtype=torch.float32, device="cuda"),
+                 amax_w=torch.zeros(w.n, dtype=torch.float32, device="cuda"))
+        R.append(d)
+
+    def phase(p, d, **kw):
+        M.adamw_step_phase(p, level, d["gq"], w.grad_fmt, d["gmeta"], d["m"], d["mmeta"], d["v"], d["w"],
+                           d["w8"], d["w8meta"], adam=adam, **kw)
+
+    for s in range(1, 5):
+        ref.fill_grads(s)
+        ref.step(s)
+        sh.fill_grads(s)
+        for d in R:
+            M.amax(d["g32"], d["gmeta"])
+        gmax = torch.stack([d["gmeta"][:, 0] for d in R]).max(0).values
+        for d in R:
+            d["gmeta"][:, 0] = gmax
+            M.quantize_fp8(d["g32"], w.grad_fmt, d["gmeta"], d["gq"])
+        for d in R:
+            phase(1, d, amax_out=d["amax_m"], step=s, **hp)
+        am = torch.stack([d["amax_m"] for d in R]).max(0).values
+        for d in R:
+            phase(2, d, amax_in=am, amax_out=d["amax_w"], step=s, **hp)
+        if level == "O3":
+            aw = torch.stack([d["amax_w"] for d in R]).max(0).values
+            for d in R:
+                phase(3, d, amax_in=aw)
+        torch.cuda.synchronize()
+        roles = ["exp_avg", "exp_avg_sq", "weights", "grad_q"] + (["weight_fp8"] if level == "O3" else [])
+        for role in roles:
+            for a, b in zip(getattr(ref, role), getattr(sh, role)):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (s, role)
+        for d in R:
+            assert torch.equal(d["gmeta"][:, :3], ref.grad_meta[:, :3]), s
+            assert torch.equal(d["mmeta"], ref.exp_avg_meta), s
+            if level == "O3":
+                assert torch.equal(d["w8meta"], ref.weight_fp8_meta), s
