@@ -491,7 +491,7 @@ def main() -> int:
         if args.warmup < 2:
             print("--graph needs --warmup >= 2 (the graphs are captured at step 2)", file=sys.stderr)
             return 2
-        st.enable_graphs(args.warmup + args.steps)
+        st.enable_graphs(args.warmup + args.steps + args.breakdown_steps)
 
     step = 0
     for _ in range(args.warmup):

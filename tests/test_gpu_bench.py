@@ -1,0 +1,49 @@
+"""bench.py end to end on a small parameter list (GPT-2-small shapes), in a
+child process: one JSON line with every key of the benchmark contract, a
+roofline record for the dominant kernel with its same-buffers ceiling, and
+the same in HIP-graph replay mode."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from tests.parity import log
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*extra):
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "gpt2_small", "--steps", "3",
+           "--warmup", "2", "--no-cpu-baseline", *extra]
+    log("running " + " ".join(cmd[1:]))
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+def test_bench_json_contract():
+    d = _run()
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 2
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["unit"] == "params/s" and d["dtype"] == "f32" and d["data"] == "synthetic"
+    assert d["config"]["params"] == 124_439_808 and "gpt2_small" in d["config"]["workload"]
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["kernel"] == "o2_pass2" and 0 < rf["frac"] < 1
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert 0 < rf["same_buffers_ceiling"]["frac"] < 1.2
+    assert set(d["kernels"]) >= {"amax", "quantize_fp8", "step_pass1", "o2_pass2"}
+
+
+def test_bench_graph_mode():
+    d = _run("--graph")
+    assert d["config"]["graph"] is True and d["value"] > 0
