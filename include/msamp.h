@@ -57,7 +57,10 @@
  *     tables are built on, and looked up for, the current device.
  *   - The caller owns every tensor and meta array. The library owns cached
  *     device tables (tensor descriptors, chunk maps, amax scratch) keyed on
- *     the pointer lists; msamp_release_cache() frees them.
+ *     the pointer lists; msamp_release_cache() frees them. The first call on
+ *     a list builds its tables (device and pinned host allocations, one
+ *     upload on the stream); at most 64 lists (512 MB of tables) are kept,
+ *     and evicting the least recently used one first waits for its device.
  *   - Calls that use the same tensor lists must be ordered (same stream, or
  *     synchronized): they share that list's amax scratch.
  *   - Entry points may be called from several host threads at once; they
