@@ -28,12 +28,18 @@ from typing import Sequence
 import torch
 
 __all__ = [
-    "E4M3", "E5M2", "MsampError", "TensorList", "lib", "amax", "quantize_fp8",
-    "quantize_fp8_prescaled",
-    "dequantize_fp8", "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
-    "codec_probe", "new_meta",
-    "allocate_state", "flat_views", "state_bytes_per_param", "profile_enable", "profile_read",
-    "KERNELS", "release_cache", "library_path",
+    "E4M3", "E5M2", "MsampError", "TensorList", "lib", "library_path", "KERNELS",
+    # gradient producer
+    "amax", "quantize_fp8", "quantize_fp8_prescaled", "dequantize_fp8",
+    # steps
+    "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
+    "step_constants", "adamw_o2_step_devconst", "adamw_o3_step_devconst", "adamw_step_phase",
+    # ablations
+    "adamw_o2_step_delayed", "adamw_o2_step_scaled_v",
+    # state helpers
+    "new_meta", "allocate_state", "flat_views", "state_bytes_per_param",
+    # measurement and test aids
+    "rmw_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
 ]
 
 E4M3 = 0
