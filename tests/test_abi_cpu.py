@@ -190,3 +190,19 @@ def test_step_constants_match_the_oracle_bit_for_bit():
                 assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (hp, step, adam, got, ref)
     with pytest.raises(M.MsampError):
         M.step_constants(step=0)
+
+
+def test_binding_declares_the_signature_of_every_header_function():
+    """Every function of include/msamp.h has explicit ctypes argument and
+    return types in the binding, with as many arguments as the header
+    declares (an undeclared ctypes call would pass 64-bit sizes and doubles
+    through C's default promotions)."""
+    text = open(os.path.join(ROOT, "include", "msamp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lib = M.lib()
+    for name, args in re.findall(r"\b(msamp_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text):
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, name
+        n_decl = 0 if args.strip() in ("", "void") else args.count(",") + 1
+        assert len(fn.argtypes) == n_decl, (name, len(fn.argtypes), n_decl)
+        assert fn.restype is not None, name
