@@ -233,18 +233,19 @@ def test_rmw_probe_leaves_every_stream_unchanged():
     assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(after, before))
 
 
-@pytest.mark.parametrize("level,adam", [("O2", False), ("O3", True)])
-def test_graph_captured_step_replays_later_steps_bit_exact(level, adam):
+@pytest.mark.parametrize("level,adam,wl", [("O2", False, "tiny_llama"), ("O3", True, "tiny_llama_o3"),
+                                           ("O2", False, "tiny_stress")])
+def test_graph_captured_step_replays_later_steps_bit_exact(level, adam, wl):
     """amax + quantize + the device-constants step captured once in a HIP
     graph (torch.cuda.graph) and replayed for steps 2..6, with the step's
     constants rewritten in device memory and new gradients written between
     replays (eager work and a synchronization in between every time). After
     every replay the whole state equals the eager by-value entry points' bit
     for bit."""
-    w = W.make("tiny_llama_o3" if level == "O3" else "tiny_llama")
+    w = W.make(wl)
     if adam:
         w.weight_decay = 0.1
-    log("graph replay %s adam=%s" % (level, adam))
+    log("graph replay %s %s adam=%s" % (wl, level, adam))
     ref = GpuState(w, "cuda", adam=adam)
     gr = GpuState(w, "cuda", adam=adam)
     consts = torch.empty(9, dtype=torch.float32, device="cuda")
@@ -332,19 +333,20 @@ def _slice_bounds(numel, ranks):
     return [[min(k, -(-(k * r // ranks) // 16) * 16) for r in range(ranks)] + [k] for k in numel]
 
 
-@pytest.mark.parametrize("level,adam", [("O2", False), ("O3", False), ("O3", True)])
-def test_sharded_phases_equal_the_unsharded_step(level, adam):
+@pytest.mark.parametrize("level,adam,wl", [("O2", False, "tiny_llama"), ("O3", False, "tiny_llama_o3"),
+                                           ("O3", True, "tiny_llama_o3"), ("O2", True, "tiny_stress")])
+def test_sharded_phases_equal_the_unsharded_step(level, adam, wl):
     """Three data-parallel ranks emulated on one GPU, each holding a slice of
     every tensor, run the split-phase step; the per-tensor amaxes are
     combined with a MAX between the phases (what an all-reduce MAX over the
     ranks would do). Over 4 steps every byte of the state and every meta
     record equals the unsharded step's."""
     ranks = 3
-    w = W.make("tiny_llama_o3" if level == "O3" else "tiny_llama")
+    w = W.make(wl)
     if adam:
         w.weight_decay = 0.1
     hp = w.hparams()
-    log("sharded phases %s adam=%s" % (level, adam))
+    log("sharded phases %s %s adam=%s" % (wl, level, adam))
     ref = GpuState(w, "cuda", adam=adam)
     sh = GpuState(w, "cuda", adam=adam)
     bounds = _slice_bounds(w.numel, ranks)
