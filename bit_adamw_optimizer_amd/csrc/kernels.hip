@@ -74,26 +74,57 @@ __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Largest value of the workgroup, folded into *dst with one atomic max. The
-// destination starts at 0 and only grows, so the atomic is skipped when the
-// value already there is at least as large: every workgroup of a tensor
-// targets the same word, and without this check ~10^5 same-address atomics
-// per launch serialize at one L2 channel.
-__device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
-  __shared__ uint32_t partial[kBlock / 64];
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (lane == 0) partial[wave] = v;
+  return v;
+}
+
+// Folds m into *dst with one atomic max. The destination starts at 0 and only
+// grows, so the atomic is skipped when the value already there is at least as
+// large: every workgroup of a tensor targets the same word, and without this
+// check ~10^5 same-address atomics per launch serialize at one L2 channel.
+__device__ __forceinline__ void atomic_max_if_larger(uint32_t m, uint32_t* dst) {
+  if (m != 0u && m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    atomicMax(dst, m);
+}
+
+// Largest value of the workgroup, folded into *dst. The closing barrier
+// keeps a later reduction of the same workgroup from overwriting the LDS
+// partials before thread 0 has read them.
+__device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
+  __shared__ uint32_t partial[kBlock / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = partial[0];
 #pragma unroll
     for (int k = 1; k < kBlock / 64; ++k) m = umax(m, partial[k]);
-    if (m != 0u && m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(dst, m);
+    atomic_max_if_larger(m, dst);
   }
+  __syncthreads();
+}
+
+// Two independent maxima of the workgroup in one reduction (separate LDS
+// slots for each), folded into *dst_a and *dst_b.
+__device__ __forceinline__ void block_max2_into(uint32_t a, uint32_t* dst_a, uint32_t b,
+                                                uint32_t* dst_b) {
+  __shared__ uint32_t partial[2][kBlock / 64];
+  a = wave_max(a);
+  b = wave_max(b);
+  if ((threadIdx.x & 63) == 0) {
+    partial[0][threadIdx.x >> 6] = a;
+    partial[1][threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    uint32_t m = partial[threadIdx.x][0];
+#pragma unroll
+    for (int k = 1; k < kBlock / 64; ++k) m = umax(m, partial[threadIdx.x][k]);
+    atomic_max_if_larger(m, threadIdx.x == 0 ? dst_a : dst_b);
+  }
+  __syncthreads();
 }
 
 // One FP8 code to binary32 (exact).
@@ -594,8 +625,7 @@ __global__ __launch_bounds__(kBlock) void k_scaled_v_pass1(const TensorDesc* __r
       }
     }
   }
-  block_max_into(mx, &amax_m[r.t]);
-  block_max_into(vx, &amax_v[r.t]);
+  block_max2_into(mx, &amax_m[r.t], vx, &amax_v[r.t]);
 }
 
 // Pass 2 of the scaled-v ablation: recompute m1, v1 identically; store m

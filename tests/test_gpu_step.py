@@ -121,6 +121,22 @@ def test_scaled_v_ablation_10_steps():
     assert_bar(stats)
 
 
+def test_scaled_v_ablation_second_moment_above_first():
+    """Pass 1 of the scaled-v ablation reduces two maxima per workgroup,
+    amax(m1) and amax(v1). At gradient scale 1000, v1 = (1-b2) g^2 exceeds
+    |m1| = (1-b1)|g| wherever |g| > 100, so amax(v1) is far above amax(m1) in
+    every workgroup: a reduction that mixed the two would store m with the
+    v scale and fail parity."""
+    w = W.make("tiny_llama")
+    w.grad_sigma = 1000.0
+    stats, gs, ost = run_parity(w, 6, scaled_v=True)
+    _report("scaled_v sigma=1000", stats)
+    assert_bar(stats)
+    for t, o in ost.items():
+        if w.numel[t] >= 1024:
+            assert o.v_meta[0] > 2.0 * o.m_meta[0], (w.names[t], o.v_meta, o.m_meta)
+
+
 def test_ragged_sizes_o2_and_o3():
     """Sizes around the 16-element vector, the 4096-element tile and the
     65536-element chunk, including empty tensors; O3 with both gradient
