@@ -47,7 +47,7 @@ def kernel_source_hash() -> str:
     counter profiles still apply to the code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_adamw_optimizer_amd", "csrc")
-    for name in ("codec.hpp", "kernels.hpp", "kernels.hip"):
+    for name in ("codec.hpp", "device.hpp", "kernels.hpp", "kernels.hip"):
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)

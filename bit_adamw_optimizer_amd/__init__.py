@@ -40,8 +40,6 @@ __all__ = [
     "new_meta", "allocate_state", "flat_views", "state_bytes_per_param",
     # measurement and test aids
     "rmw_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
-    # step schedule
-    "SCHEDULES", "set_step_schedule", "get_step_schedule", "step_wait_timeouts",
 ]
 
 E4M3 = 0
@@ -56,10 +54,7 @@ PROBE_F16_TO_F32 = 5
 
 # kernel kinds of msamp_profile_read, in enum order
 KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
-           "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe", "o2_step", "o3_step"]
-
-# step schedules (msamp_step_schedule)
-SCHEDULES = {"persistent": 0, "passes": 1}
+           "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
@@ -150,12 +145,6 @@ def lib():
         L.msamp_adamw_o3_step_devconst.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                                    vp, vp, ctypes.c_int, vp]
         L.msamp_adamw_o3_step_devconst.restype = st
-        L.msamp_set_step_schedule.argtypes = [ctypes.c_int]
-        L.msamp_set_step_schedule.restype = st
-        L.msamp_get_step_schedule.argtypes = []
-        L.msamp_get_step_schedule.restype = ctypes.c_int
-        L.msamp_step_wait_timeouts.argtypes = [ctypes.POINTER(i64)]
-        L.msamp_step_wait_timeouts.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
@@ -545,28 +534,6 @@ def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:
 
 def release_cache() -> None:
     _check(lib().msamp_release_cache())
-
-
-def set_step_schedule(name: str) -> None:
-    """Selects how the O2/O3 steps are launched: "persistent" (default: the
-    whole step in one cooperative launch) or "passes" (one launch per pass).
-    Both give bit-identical results (see msamp_set_step_schedule)."""
-    if name not in SCHEDULES:
-        raise ValueError("schedule must be one of %s" % sorted(SCHEDULES))
-    _check(lib().msamp_set_step_schedule(SCHEDULES[name]))
-
-
-def get_step_schedule() -> str:
-    v = int(lib().msamp_get_step_schedule())
-    return {i: k for k, i in SCHEDULES.items()}[v]
-
-
-def step_wait_timeouts() -> int:
-    """Waits for the devices, then returns (and resets) the number of waits
-    of the persistent step that gave up; 0 in normal operation."""
-    n = ctypes.c_int64(0)
-    _check(lib().msamp_step_wait_timeouts(ctypes.byref(n)))
-    return int(n.value)
 
 
 def profile_enable(on: bool) -> None:

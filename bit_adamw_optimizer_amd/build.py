@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libmsamp.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "persistent.hip"), os.path.join(CSRC, "abi.hip")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "abi.hip")]
 HEADERS = [os.path.join(CSRC, "codec.hpp"), os.path.join(CSRC, "device.hpp"), os.path.join(CSRC, "kernels.hpp"),
            os.path.join(INCLUDE, "msamp.h")]
 

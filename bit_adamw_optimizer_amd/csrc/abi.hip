@@ -9,7 +9,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstddef>
 #include <cmath>
 #include <cstdio>
@@ -108,9 +107,8 @@ hipError_t timed(msamp_kernel_kind kind, hipStream_t s, F&& launch) {
 enum PlanKind : uint64_t { kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3 };
 
 // Device tables of one tensor list: amax scratch (two u32 per tensor, kept
-// at zero between calls), the persistent step's scratch (eight u32 per
-// tensor, also zero between calls) and error word, the descriptors and the
-// chunk map, in one allocation uploaded once from pinned host memory.
+// at zero between calls), the descriptors and the chunk map, in one
+// allocation uploaded once from pinned host memory.
 struct Plan {
   int device = -1;
   std::vector<uint64_t> key;
@@ -119,8 +117,6 @@ struct Plan {
   size_t bytes = 0;
   uint32_t* scratch_a = nullptr;
   uint32_t* scratch_b = nullptr;
-  uint32_t* pscr = nullptr;  // persistent step: kPersistentScratchWords per tensor
-  uint32_t* perr = nullptr;  // persistent step: wait time-outs
   TensorDesc* desc = nullptr;
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
@@ -234,11 +230,6 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     total += k;
   }
   if (total > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks for one launch");
-  {
-    int64_t tiles = 0;
-    for (int32_t t = 0; t < n; ++t) tiles += (numel[t] + kPersistentTile - 1) / kPersistentTile;
-    if (tiles > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many tiles for one launch");
-  }
   chunks.reserve((size_t)total);
   for (int32_t t = 0; t < n; ++t) {
     int64_t k = (numel[t] + kChunk - 1) / kChunk;
@@ -249,9 +240,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   auto plan = std::make_unique<Plan>();
   plan->device = dev;
   plan->key = std::move(key);
-  const size_t pscr_words = (size_t)kPersistentScratchWords * (size_t)std::max(n, 1);
-  const size_t scratch_bytes =
-      align_up(sizeof(uint32_t) * (2 * (size_t)std::max(n, 1) + pscr_words), 256) + 256;
+  const size_t scratch_bytes = align_up(sizeof(uint32_t) * 2 * (size_t)std::max(n, 1), 256);
   const size_t desc_bytes = align_up(sizeof(TensorDesc) * (size_t)std::max(n, 1), 256);
   const size_t chunk_bytes = align_up(sizeof(ChunkRef) * std::max<size_t>(chunks.size(), 1), 256);
   plan->bytes = scratch_bytes + desc_bytes + chunk_bytes;
@@ -271,14 +260,10 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   char* hb = (char*)plan->host;
   std::memset(hb, 0, plan->bytes);
   TensorDesc* hd = (TensorDesc*)(hb + scratch_bytes);
-  int64_t tile_start = 0;
   for (int32_t t = 0; t < n; ++t) {
     TensorDesc d;
     std::memset(&d, 0, sizeof d);
     d.numel = numel[t];
-    d.reserved[0] = (numel[t] + kPersistentTile - 1) / kPersistentTile;
-    d.reserved[1] = tile_start;
-    tile_start += d.reserved[0];
     const void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
     for (int r = 0; r < nroles && r < 5; ++r) p[r] = ptrs[r][t];
     d.p0 = p[0];
@@ -294,8 +279,6 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   char* db = (char*)plan->dev;
   plan->scratch_a = (uint32_t*)db;
   plan->scratch_b = (uint32_t*)db + std::max(n, 1);
-  plan->pscr = (uint32_t*)db + 2 * (size_t)std::max(n, 1);
-  plan->perr = (uint32_t*)(db + scratch_bytes - 256);
   plan->desc = (TensorDesc*)(db + scratch_bytes);
   plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
   plan->nchunks = (int64_t)chunks.size();
@@ -311,57 +294,6 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   // Never evict the plan just returned: it is the most recently used.
   evict_locked(c);
   *lease = std::move(lk);
-  return MSAMP_OK;
-}
-
-// ------------------------------------------------- persistent schedule ---
-
-std::atomic<int> g_schedule{MSAMP_SCHEDULE_PERSISTENT};
-
-// Workgroups of the persistent step per device: one per compute unit
-// (0 = not known yet).
-struct DeviceGrid {
-  std::mutex mu;
-  std::vector<unsigned> grid;
-};
-
-DeviceGrid& device_grid() {
-  static DeviceGrid* g = new DeviceGrid();
-  return *g;
-}
-
-msamp_status persistent_grid(int dev, unsigned* out) {
-  DeviceGrid& g = device_grid();
-  std::lock_guard<std::mutex> lk(g.mu);
-  if ((size_t)dev < g.grid.size() && g.grid[(size_t)dev] != 0) {
-    *out = g.grid[(size_t)dev];
-    return MSAMP_OK;
-  }
-  int cus = 0, coop = 0, occ = 0;
-  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(compute units)");
-  e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-  if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(cooperative launch)");
-  if (!coop) return fail(MSAMP_E_HIP, "the device does not support cooperative launches");
-  e = persistent_occupancy(&occ);
-  if (e != hipSuccess) return fail_hip(e, "occupancy of the persistent step");
-  if (occ < 1 || cus < 1) return fail(MSAMP_E_HIP, "the persistent step does not fit on a compute unit");
-  if (g.grid.size() <= (size_t)dev) g.grid.resize((size_t)dev + 1, 0u);
-  g.grid[(size_t)dev] = (unsigned)cus;
-  *out = (unsigned)cus;
-  return MSAMP_OK;
-}
-
-// True when the persistent schedule runs this call: selected, and the
-// stream is not being captured into a graph (cooperative launches are not
-// captured; the pass-per-launch schedule gives bit-identical results).
-msamp_status use_persistent(hipStream_t s, bool* out) {
-  *out = false;
-  if (g_schedule.load() != MSAMP_SCHEDULE_PERSISTENT) return MSAMP_OK;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  hipError_t e = hipStreamIsCapturing(s, &cs);
-  if (e != hipSuccess) return fail_hip(e, "hipStreamIsCapturing");
-  *out = cs == hipStreamCaptureStatusNone;
   return MSAMP_OK;
 }
 
@@ -511,16 +443,6 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   MSAMP_TRY(step_plan(o3, n, numel, grad, exp_avg, exp_avg_sq, weight, weight_fp8, s, &p, &lease));
   const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
 
-  bool persistent = false;
-  MSAMP_TRY(use_persistent(s, &persistent));
-  if (persistent) {
-    unsigned grid = 0;
-    MSAMP_TRY(persistent_grid(p->device, &grid));
-    MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_STEP : MSAMP_KERNEL_O2_STEP, s,
-                 launch_step_persistent(grad_fmt, o3, coupled, grid, p->desc, n, grad_meta, exp_avg_meta,
-                                        weight_fp8_meta, p->pscr, p->perr, k, s, kdev));
-    return MSAMP_OK;
-  }
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, k, s, kdev));
@@ -689,8 +611,6 @@ const char* msamp_kernel_name(msamp_kernel_kind kind) {
     case MSAMP_KERNEL_AMAX_FINALIZE: return "amax_finalize";
     case MSAMP_KERNEL_O2_DELAYED: return "o2_delayed";
     case MSAMP_KERNEL_RMW_PROBE: return "rmw_probe";
-    case MSAMP_KERNEL_O2_STEP: return "o2_step";
-    case MSAMP_KERNEL_O3_STEP: return "o3_step";
     default: return "";
   }
 }
@@ -949,47 +869,6 @@ msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const
   return guarded([&]() {
     return step_scaled_v_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                               exp_avg_sq, exp_avg_sq_meta, weight, hp, step, stream);
-  });
-}
-
-msamp_status msamp_set_step_schedule(msamp_step_schedule schedule) {
-  return guarded([&]() -> msamp_status {
-    g_last_error.clear();
-    if (schedule != MSAMP_SCHEDULE_PERSISTENT && schedule != MSAMP_SCHEDULE_PASSES)
-      return fail(MSAMP_E_INVALID_ARG, "unknown step schedule");
-    g_schedule.store((int)schedule);
-    return MSAMP_OK;
-  });
-}
-
-msamp_step_schedule msamp_get_step_schedule(void) { return (msamp_step_schedule)g_schedule.load(); }
-
-msamp_status msamp_step_wait_timeouts(int64_t* count) {
-  return guarded([&]() -> msamp_status {
-    g_last_error.clear();
-    if (count == nullptr) return fail(MSAMP_E_INVALID_ARG, "count is NULL");
-    PlanCache& c = cache();
-    std::lock_guard<std::mutex> lk(c.mu);
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    int64_t total = 0;
-    msamp_status st = MSAMP_OK;
-    for (auto& kv : c.map)
-      for (auto& p : kv.second) {
-        uint32_t v = 0;
-        hipError_t e = hipSetDevice(p->device);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipMemcpy(&v, p->perr, sizeof v, hipMemcpyDeviceToHost);
-        if (e == hipSuccess && v != 0) e = hipMemset(p->perr, 0, sizeof v);
-        if (e != hipSuccess) {
-          st = fail_hip(e, "reading the wait time-out count");
-          break;
-        }
-        total += v;
-      }
-    if (cur >= 0) (void)hipSetDevice(cur);
-    *count = total;
-    return st;
   });
 }
 

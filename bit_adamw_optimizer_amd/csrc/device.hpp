@@ -1,7 +1,7 @@
-// device.hpp -- device-side helpers shared by the multi-tensor kernels
-// (kernels.hip) and the persistent step kernel (persistent.hip): global
-// address-space loads and stores, workgroup max reductions, packed FP8/FP16
-// conversions of 8 elements, and the AdamW arithmetic of one element.
+// device.hpp -- device-side helpers of the multi-tensor kernels
+// (kernels.hip): global address-space loads and stores, workgroup max
+// reductions, packed FP8/FP16 conversions of 8 elements, and the AdamW
+// arithmetic of one element.
 //
 // The AdamW arithmetic is binary32 with exactly the operation order of the
 // definition in msamp.h; files including this header are compiled with

@@ -16,19 +16,8 @@ constexpr int kBlock = 256;
 constexpr int64_t kTile = (int64_t)kBlock * 16;
 constexpr int64_t kChunk = 16 * kTile;  // 65536 elements
 
-// The persistent step (persistent.hip): one cooperative launch of one
-// workgroup of kPersistentBlock threads per compute unit, tiles of
-// kPersistentTile elements, and kPersistentScratchWords u32 of scratch per
-// tensor (zero between calls).
-constexpr int kPersistentBlock = 512;
-constexpr int64_t kPersistentTile = (int64_t)kPersistentBlock * 16;  // 8192 elements
-constexpr int kPersistentScratchWords = 8;
-
-// Multi-tensor-apply descriptor of one tensor (64 bytes). reserved[0] holds
-// the tensor's number of kPersistentTile tiles and reserved[1] the number of
-// such tiles of the tensors before it in the list (the persistent step
-// assigns tile k of the tensor to workgroup (reserved[1] + k) mod grid). The
-// roles of the pointers depend on the operation:
+// Multi-tensor-apply descriptor of one tensor (64 bytes). The roles of the
+// pointers depend on the operation:
 //                 p0 (read)     p1            p2           p3          p4
 //   amax          x f32         -             -            -           -
 //   quantize      x f32         q u8 (out)    -            -           -
@@ -112,18 +101,6 @@ hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64
 hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
                                 uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
                                 hipStream_t stream);
-// The whole O2 (o3 = false) or O3 step in one cooperative launch of 'grid'
-// workgroups (at most one per compute unit may be resident at once for the
-// launch to be accepted): the passes of every tensor, its meta records
-// (mmeta, and wmeta for O3) and the reset of its scratch words 'scr'. A wait
-// that times out adds 1 to *err. Constants by value (k), or from device
-// memory when kdev is not null.
-hipError_t launch_step_persistent(int gfmt, bool o3, bool coupled, unsigned grid, const TensorDesc* desc,
-                                  int32_t n, const msamp_meta* gmeta, msamp_meta* mmeta, msamp_meta* wmeta,
-                                  uint32_t* scr, uint32_t* err, const StepConsts& k, hipStream_t stream,
-                                  const StepConsts* kdev = nullptr);
-// Resident workgroups per compute unit of the persistent step kernel.
-hipError_t persistent_occupancy(int* blocks_per_cu);
 hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipStream_t stream);
 // Split-phase steps: out[t] <- amax[t] as binary32 and amax[t] <- 0; and
 // meta[t] <- {a, scale(a, fmax), 1/scale, 0} from a caller's amax array.

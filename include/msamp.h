@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define MSAMP_ABI_VERSION 2
+#define MSAMP_ABI_VERSION 3
 
 typedef enum {
   MSAMP_OK = 0,
@@ -197,12 +197,6 @@ msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int6
  * Two passes: 13 bytes per element (read g, m; then read g, m, v, w and
  * write m, v, w). Non-finite gradient codes are outside the contract (the
  * caller skips such steps, as GradScaler does in [RD] "Usage").
- * Schedule (msamp_set_step_schedule): by default the whole step is ONE
- * cooperative launch that holds one workgroup on every compute unit of the
- * device until it ends; pass 2 of a tensor waits for every workgroup's
- * pass 1 of it, with a bounded wait (msamp_step_wait_timeouts). The results
- * are bit-identical to the schedule of one launch per pass, which is used
- * instead while the stream is being captured into a graph.
  */
 msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t* const* grad,
                                  msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
@@ -375,28 +369,6 @@ msamp_status msamp_adamw_o3_step_phase3(int32_t n, const int64_t* numel, const u
                                         uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                         const float* amax_w, void* stream);
 
-/* Schedules of the O2/O3 steps (msamp_adamw_o2_step, msamp_adamw_o3_step,
- * msamp_adam_o2_step, msamp_adam_o3_step and the *_devconst steps); both
- * give bit-identical results:
- *   MSAMP_SCHEDULE_PERSISTENT  (default) one cooperative launch for the
- *       whole step: per tensor, pass 1 over every workgroup's tiles, a wait
- *       on a per-tensor counter, then pass 2 (and O3's pass 3) on the same
- *       tensor while its codes are still cached; meta records written by the
- *       workgroup that completes the tensor.
- *   MSAMP_SCHEDULE_PASSES  one multi-tensor launch per pass over the whole
- *       list, then a meta-finalize launch.
- * The setting is process-wide; it is read when a step is enqueued. */
-typedef enum { MSAMP_SCHEDULE_PERSISTENT = 0, MSAMP_SCHEDULE_PASSES = 1 } msamp_step_schedule;
-msamp_status msamp_set_step_schedule(msamp_step_schedule schedule);
-msamp_step_schedule msamp_get_step_schedule(void);
-
-/* Waits for every device the library has tables on, then returns in *count
- * the number of waits of the persistent schedule that gave up since the
- * last call (and resets it). A wait gives up only if the other workgroups
- * make no progress for a long time (about 10^5 polls); the results of that
- * step are then undefined. 0 in normal operation. */
-msamp_status msamp_step_wait_timeouts(int64_t* count);
-
 /* Frees every cached device table of the library (all devices) after
  * waiting for the devices to finish. Safe to call at any time from one
  * thread while no other library call runs. */
@@ -454,9 +426,7 @@ typedef enum {
   MSAMP_KERNEL_AMAX_FINALIZE = 8, /* amax write-back of msamp_amax */
   MSAMP_KERNEL_O2_DELAYED = 9,  /* one-pass delayed-scaling ablation */
   MSAMP_KERNEL_RMW_PROBE = 10,  /* msamp_rmw_probe (measurement aid) */
-  MSAMP_KERNEL_O2_STEP = 11,    /* O2 step, persistent schedule (all passes) */
-  MSAMP_KERNEL_O3_STEP = 12,    /* O3 step, persistent schedule (all passes) */
-  MSAMP_KERNEL_COUNT = 13
+  MSAMP_KERNEL_COUNT = 11
 } msamp_kernel_kind;
 
 /* on != 0 starts recording (and discards earlier records; the events for

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msamp_abi_version() == 2
+    assert lib.msamp_abi_version() == 3
 
 
 def test_library_is_built_for_gfx950():

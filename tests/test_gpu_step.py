@@ -20,14 +20,6 @@ def _report(name, stats):
                                   for k, s in stats.items() if s.total))
 
 
-@pytest.fixture(autouse=True)
-def _default_schedule():
-    M.set_step_schedule("persistent")
-    yield
-    M.set_step_schedule("persistent")
-    assert M.step_wait_timeouts() == 0
-
-
 def test_single_1m_o2_10_steps():
     w = W.make("single_1m")
     log("single_1m O2, %d params, 10 steps" % w.params)
@@ -36,21 +28,17 @@ def test_single_1m_o2_10_steps():
     assert_bar(stats)
 
 
-@pytest.mark.parametrize("schedule", ["persistent", "passes"])
-def test_tiny_llama_o2_10_steps(schedule):
-    M.set_step_schedule(schedule)
+def test_tiny_llama_o2_10_steps():
     w = W.make("tiny_llama")
-    log("tiny_llama O2 (%s), %d tensors, %d params" % (schedule, w.n, w.params))
+    log("tiny_llama O2, %d tensors, %d params" % (w.n, w.params))
     stats, _, _ = run_parity(w, 10)
     _report("tiny_llama", stats)
     assert_bar(stats)
 
 
-@pytest.mark.parametrize("schedule", ["persistent", "passes"])
-def test_tiny_llama_o3_10_steps(schedule):
-    M.set_step_schedule(schedule)
+def test_tiny_llama_o3_10_steps():
     w = W.make("tiny_llama_o3")
-    log("tiny_llama O3 (%s), %d tensors, %d params" % (schedule, w.n, w.params))
+    log("tiny_llama O3, %d tensors, %d params" % (w.n, w.params))
     stats, _, _ = run_parity(w, 10)
     _report("tiny_llama_o3", stats)
     assert_bar(stats)
@@ -149,14 +137,11 @@ def test_scaled_v_ablation_second_moment_above_first():
             assert o.v_meta[0] > 2.0 * o.m_meta[0], (w.names[t], o.v_meta, o.m_meta)
 
 
-@pytest.mark.parametrize("schedule", ["persistent", "passes"])
-def test_ragged_sizes_o2_and_o3(schedule):
-    """Sizes around the 16-element vector, the 4096- and 8192-element tiles
-    and the 65536-element chunk, including empty tensors; O3 with both
-    gradient formats."""
-    M.set_step_schedule(schedule)
-    sizes = [0, 1, 7, 15, 16, 17, 31, 4095, 4096, 4097, 8191, 8192, 8193, 16385, 65535, 65536, 65537,
-             131072 + 4096 + 9, 0, 3]
+def test_ragged_sizes_o2_and_o3():
+    """Sizes around the 16-element vector, the 4096-element tile and the
+    65536-element chunk, including empty tensors; O3 with both gradient
+    formats."""
+    sizes = [0, 1, 7, 15, 16, 17, 31, 4095, 4096, 4097, 65535, 65536, 65537, 131072 + 4096 + 9, 0, 3]
     for level, fmt in (("O2", W.E4M3), ("O3", W.E4M3), ("O3", W.E5M2)):
         w = W.Workload("ragged_%s_%d" % (level, fmt), level, fmt, 4, ["t%d" % i for i in range(len(sizes))],
                        sizes, lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.05, seed_base=11)
@@ -168,34 +153,6 @@ def test_ragged_sizes_o2_and_o3(schedule):
         for t, k in enumerate(sizes):
             if k == 0:
                 assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
-
-
-@pytest.mark.parametrize("level,adam,wl", [("O2", False, "tiny_stress"), ("O3", False, "tiny_llama_o3"),
-                                           ("O2", True, "tiny_llama"), ("O3", True, "tiny_llama_o3")])
-def test_schedules_are_bit_identical(level, adam, wl):
-    """The persistent schedule (one cooperative launch per step) and the
-    schedule of one launch per pass leave every byte of the state and every
-    meta record identical, step after step."""
-    w = W.make(wl)
-    w.level = level
-    states = {}
-    for sched in ("persistent", "passes"):
-        M.set_step_schedule(sched)
-        gs = GpuState(w, "cuda", adam=adam)
-        snaps = []
-        for s in range(1, 5):
-            gs.fill_grads(s)
-            gs.step(s)
-            parts = gs.exp_avg + gs.exp_avg_sq + gs.weights + [gs.exp_avg_meta]
-            if level == "O3":
-                parts += gs.weight_fp8 + [gs.weight_fp8_meta]
-            snaps.append([x.clone() for x in parts])
-        torch.cuda.synchronize()
-        states[sched] = snaps
-    for s, (a, b) in enumerate(zip(states["persistent"], states["passes"]), 1):
-        for i, (x, y) in enumerate(zip(a, b)):
-            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (wl, level, adam, s, i)
-    log("%s %s adam=%s: schedules identical over 4 steps" % (wl, level, adam))
 
 
 def test_gpt2_small_o2_10_steps():
