@@ -4,7 +4,11 @@
 One step = one pass of the whole path over one batch of synthetic input:
 per-tensor amax of the binary32 gradients, their saturating FP8 quantize,
 then the low-precision AdamW step (O2: two passes + meta finalize; O3: three
-passes + finalize), all through the C ABI of libmsamp.so. Inputs (weights,
+passes + finalize), all through the C ABI of libmsamp.so. By default the
+quantize runs in the same pass as the step's pass 1
+(msamp_quantize_adamw_o2_step / _o3_step: 21 bytes per parameter for O2
+instead of 22); --separate-quantize runs msamp_quantize_fp8 and the step as
+two calls. Inputs (weights,
 states and two sets of binary32 gradients, alternated between steps) are
 resident in HBM before the timed region starts.
 
@@ -39,6 +43,7 @@ GRAD_QUANTIZE_BYTES = 4 + 1  # read f32, write FP8
 PASS1_BYTES = 1 + 1          # read grad FP8, exp_avg FP8
 PASS2_BYTES = 6 + 5          # read g, m, v, w; write m, v, w
 PASS3_BYTES = 2 + 1          # read master FP16, write FP8 copy
+QUANTIZE_PASS1_BYTES = 4 + 1 + 1  # read f32 grad, exp_avg FP8; write grad FP8
 
 
 def kernel_source_hash() -> str:
@@ -68,6 +73,10 @@ def parse():
                    help="adamw (decoupled decay, default), adam (coupled L2), or the O2-only "
                         "ablations adamw-delayed (one-pass delayed scaling) and adamw-scaled-v "
                         "(per-tensor-scaled FP16 second moment)")
+    p.add_argument("--separate-quantize", action="store_true",
+                   help="run the gradient quantize and the AdamW step as two calls (the default "
+                        "fuses the quantize into pass 1 of the step; Adam and the ablations always "
+                        "run the two calls)")
     p.add_argument("--shard", type=int, default=1,
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,7 +114,7 @@ class State:
     """Device state of a workload plus two resident binary32 gradient sets."""
 
     def __init__(self, w, device, adam: bool = False, delayed: bool = False,
-                 scaled_v: bool = False):
+                 scaled_v: bool = False, fused: bool = False):
         import torch
 
         import bit_adamw_optimizer_amd as M
@@ -115,9 +124,17 @@ class State:
         self.adam = adam
         self.delayed = delayed
         self.scaled_v = scaled_v
+        self.fused = fused  # gradient quantize fused with pass 1 of the AdamW step
         self.exp_avg_sq_meta = M.new_meta(w.n, device) if scaled_v else None
-        # every role lives in one allocation (views per tensor)
-        self.weights = W.init_weights(w, device, out=M.flat_views(w.numel, torch.float16, device))
+        # every role lives in one allocation (views per tensor). Lists of many
+        # tensors without per-tensor factors draw their inputs over the whole
+        # allocation in a few launches instead of a few per tensor.
+        flat_gen = w.n > 1000 and w.factor is None
+        self.weights = M.flat_views(w.numel, torch.float16, device)
+        if flat_gen:
+            W.init_weights_flat(w, self.weights, device)
+        else:
+            W.init_weights(w, device, out=self.weights)
         st = M.allocate_state(self.weights, w.level, flat=True)
         self.exp_avg_meta = st["exp_avg_meta"]
         self.weight_fp8_meta = st.get("weight_fp8_meta")
@@ -130,8 +147,11 @@ class State:
         self.grad_sets = []
         for s in (1, 2):
             g = M.flat_views(w.numel, torch.float32, device)
-            for t in range(w.n):
-                W.grad_tensor(w, t, s, device, out=g[t])
+            if flat_gen:
+                W.grads_flat(w, s, g, device)
+            else:
+                for t in range(w.n):
+                    W.grad_tensor(w, t, s, device, out=g[t])
             self.grad_sets.append(M.TensorList(g, "f32", "grad_f32"))
         torch.cuda.synchronize()
 
@@ -189,6 +209,15 @@ class State:
                 self.graphs[(step - 1) % 2].replay()
             return
         M.amax(g32, self.grad_meta)
+        if self.fused:
+            if w.level == "O2":
+                M.quantize_adamw_o2_step(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
+            else:
+                M.quantize_adamw_o3_step(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
+                                         self.weight_fp8_meta, step=step, **w.hparams())
+            return
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2" and self.scaled_v:
             M.adamw_o2_step_scaled_v(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m,
@@ -204,6 +233,14 @@ class State:
             fn = M.adam_o3_step if self.adam else M.adamw_o3_step
             fn(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m, self.exp_avg_meta,
                self.tl_v, self.tl_w, self.tl_w8, self.weight_fp8_meta, step=step, **w.hparams())
+
+
+def storage_of(views):
+    """The one allocation behind a list of views (flat_views)."""
+    import torch
+
+    base = views[0]
+    return torch.empty(0, dtype=base.dtype, device=base.device).set_(base.untyped_storage())
 
 
 def numerics_report(st) -> dict:
@@ -297,6 +334,8 @@ def _kind_of(name: str):
         return ("o3_pass2" if len(targs) > 1 and targs[1] == "true" else "o2_pass2"), PASS2_BYTES
     if fn == "k_o3_pass3":
         return "o3_pass3", PASS3_BYTES
+    if fn == "k_quantize_pass1":
+        return "quantize_pass1", QUANTIZE_PASS1_BYTES
     if fn == "k_rmw_probe":
         return "rmw_probe", PASS2_BYTES
     if fn == "k_scaled_v_pass1":  # also reads the FP16 second moment
@@ -483,7 +522,8 @@ def main() -> int:
     if (delayed or scaled_v) and w.level != "O2":
         print("the %s ablation exists for the O2 layout only" % args.optimizer, file=sys.stderr)
         return 2
-    st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v)
+    fused = not (args.separate_quantize or adam or delayed or scaled_v or args.graph)
+    st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, fused=fused)
     if args.graph:
         if delayed or scaled_v:
             print("--graph covers the AdamW and Adam steps only", file=sys.stderr)
@@ -544,6 +584,25 @@ def main() -> int:
         M.profile_enable(False)
         n_p, ms_p = M.profile_read("rmw_probe")
         probe_ms = ms_p / n_p if n_p else None
+    # plain read and copy streams over the run's own binary32 gradient
+    # buffers (4 bytes per parameter each; the timed steps are done, so the
+    # second set may be overwritten)
+    streams = {}
+    if not args.no_profile:
+        g0, g1 = (storage_of(gs.tensors) for gs in st.grad_sets)
+        nb = (g0.numel() * 4) // 16 * 16
+        M.profile_enable(True)
+        for _ in range(5):
+            M.stream_probe(g0)
+        for _ in range(5):
+            M.stream_probe(g0, g1)
+        torch.cuda.synchronize()
+        M.profile_enable(False)
+        for kind, moved in (("read_probe", nb), ("copy_probe", 2 * nb)):
+            n_p, ms_p = M.profile_read(kind)
+            if n_p:
+                streams[kind] = {"bytes": moved, "ms": round(ms_p / n_p, 4),
+                                 "GB/s": round(moved / (ms_p / n_p * 1e-3) / 1e9, 1)}
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     P = w.params
@@ -551,11 +610,18 @@ def main() -> int:
     # (and so does the scaled-v ablation's, for its amax(v1))
     pass1_bytes = PASS1_BYTES + (2 if adam or scaled_v else 0)
     step_bytes = (0 if delayed else pass1_bytes) + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
-    path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
+    if fused:
+        # the quantize writes the codes and pass 1 takes them from registers:
+        # one launch reads the f32 gradient and the first moment, writes the codes
+        step_bytes = QUANTIZE_PASS1_BYTES + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+        path_bytes = GRAD_AMAX_BYTES + step_bytes
+    else:
+        path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
     gbps = path_bytes * P / (ms_per_step * 1e-3) / 1e9
 
     per_kernel_bytes = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES,
                         "step_pass1": pass1_bytes, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
+                        "quantize_pass1": QUANTIZE_PASS1_BYTES,
                         "o3_pass3": PASS3_BYTES, "o2_delayed": PASS2_BYTES}
     breakdown = {}
     for k, d in kernels.items():
@@ -577,7 +643,20 @@ def main() -> int:
                 "GB/s": round(ceiling, 1), "frac": round(achieved / ceiling, 4),
                 "probe": "msamp_rmw_probe: the update pass's loads and stores (read 6, write 5 B/p) "
                          "without arithmetic, on the same buffers, %.4f ms" % probe_ms}
-    opt_ms = sum(kernels[k]["avg_ms"] for k in ("step_pass1", dom, "o3_pass3", "finalize")
+        # what the memory system gives plain traffic shapes on this run's
+        # buffers: a pure read, a copy, and the update pass's read/write mix
+        ceil = {}
+        if "read_probe" in streams:
+            ceil["read"] = dict(streams["read_probe"], probe="msamp_stream_probe READ over the f32 gradients")
+        if "copy_probe" in streams:
+            ceil["copy"] = dict(streams["copy_probe"], probe="msamp_stream_probe COPY between the two f32 "
+                                                            "gradient sets (bytes = read + written)")
+        if probe_ms:
+            ceil["update_pass_mix"] = {"bytes": PASS2_BYTES * P, "ms": round(probe_ms, 4),
+                                       "GB/s": round(PASS2_BYTES * P / (probe_ms * 1e-3) / 1e9, 1),
+                                       "probe": "msamp_rmw_probe (read 6, write 5 B/p)"}
+        roofline["ceilings"] = ceil
+    opt_ms = sum(kernels[k]["avg_ms"] for k in ("step_pass1", "quantize_pass1", dom, "o3_pass3", "finalize")
                  if k in kernels)
     result = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) for O2/O3 FP8 AdamW step",
@@ -593,7 +672,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s FP8 %s step, %d tensors, %d params, %s grads "
-                               "(amax + quantize + step per iteration%s)"
+                               "(amax + quantize + step per iteration%s%s)"
                                % (w.name, w.level, {"adam": "Adam", "adamw": "AdamW",
                                                     "adamw-delayed": "AdamW one-pass delayed-scaling "
                                                                      "ablation",
@@ -601,16 +680,18 @@ def main() -> int:
                                                                       "ablation"}[args.optimizer],
                                   w.n, P,
                                   "E4M3" if w.grad_fmt == 0 else "E5M2",
-                                  ", HIP-graph replay" if args.graph else ""),
+                                  ", HIP-graph replay" if args.graph else "",
+                                  ", quantize fused with pass 1" if fused else ""),
                    "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P,
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "fused_quantize": fused},
         "hbm_gbps": round(gbps, 1),
         "pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_param": path_bytes,
         "optimizer_step": {"ms": round(opt_ms, 4) if kernels else None,
                            "params_per_s": P / (opt_ms * 1e-3) if kernels else None,
                            "GB/s": round(step_bytes * P / (opt_ms * 1e-3) / 1e9, 1) if kernels else None,
-                           "bytes_per_param": step_bytes},
+                           "bytes_per_param": step_bytes,
+                           "includes_grad_quantize": fused},
         "kernels": breakdown,
         "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),

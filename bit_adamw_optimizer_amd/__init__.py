@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Sequence
+from typing import Optional, Sequence
 
 import torch
 
@@ -34,12 +34,13 @@ __all__ = [
     # steps
     "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
     "step_constants", "adamw_o2_step_devconst", "adamw_o3_step_devconst", "adamw_step_phase",
+    "quantize_adamw_o2_step", "quantize_adamw_o3_step",
     # ablations
     "adamw_o2_step_delayed", "adamw_o2_step_scaled_v",
     # state helpers
     "new_meta", "allocate_state", "flat_views", "state_bytes_per_param",
     # measurement and test aids
-    "rmw_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
+    "rmw_probe", "stream_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
 ]
 
 E4M3 = 0
@@ -54,7 +55,8 @@ PROBE_F16_TO_F32 = 5
 
 # kernel kinds of msamp_profile_read, in enum order
 KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
-           "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe"]
+           "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe", "quantize_pass1",
+           "read_probe", "copy_probe"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
@@ -115,6 +117,12 @@ def lib():
         L.msamp_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(_HParams), i64, vp]
         L.msamp_adamw_o3_step.restype = st
+        L.msamp_quantize_adamw_o2_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.POINTER(_HParams), i64, vp]
+        L.msamp_quantize_adamw_o2_step.restype = st
+        L.msamp_quantize_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, ctypes.POINTER(_HParams), i64, vp]
+        L.msamp_quantize_adamw_o3_step.restype = st
         L.msamp_adam_o2_step.argtypes = L.msamp_adamw_o2_step.argtypes
         L.msamp_adam_o2_step.restype = st
         L.msamp_adam_o3_step.argtypes = L.msamp_adamw_o3_step.argtypes
@@ -134,6 +142,8 @@ def lib():
         L.msamp_adamw_o3_step_phase3.argtypes = o3_args + [vp, vp]
         for f in ("o2_step_phase1", "o2_step_phase2", "o3_step_phase1", "o3_step_phase2", "o3_step_phase3"):
             getattr(L, "msamp_adamw_" + f).restype = st
+        L.msamp_stream_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
+        L.msamp_stream_probe.restype = st
         L.msamp_rmw_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp]
         L.msamp_rmw_probe.restype = st
         L.msamp_step_constants_compute.argtypes = [ctypes.POINTER(_HParams), i64, ctypes.c_int,
@@ -349,6 +359,53 @@ def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
             ctypes.byref(hp), int(step), _stream(g.device)))
 
 
+def quantize_adamw_o2_step(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq,
+                           weight, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                           step: int) -> None:
+    """Gradient quantize fused with the O2 AdamW step (see include/msamp.h):
+    grad_meta must hold the gradient amax; grad receives the FP8 codes."""
+    _quantize_step("O2", grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                   None, None, _hp(lr, betas, eps, weight_decay), step)
+
+
+def quantize_adamw_o3_step(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq,
+                           master, weight_fp8, weight_fp8_meta, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
+                           weight_decay=0.01, step: int) -> None:
+    """Gradient quantize fused with the O3 AdamW step (see include/msamp.h)."""
+    _quantize_step("O3", grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, master,
+                   weight_fp8, weight_fp8_meta, _hp(lr, betas, eps, weight_decay), step)
+
+
+def _quantize_step(level, grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                   weight_fp8, weight_fp8_meta, hp, step) -> None:
+    x = _tl(grad_f32, "f32", "grad_f32")
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight" if level == "O2" else "master")
+    lists = [(g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")]
+    w8 = None
+    if level == "O3":
+        w8 = _tl(weight_fp8, "u8", "weight_fp8")
+        lists.append((w8, "weight_fp8"))
+    for other, name in lists:
+        x.matches(other, name)
+    if x.n == 0:
+        return
+    with torch.cuda.device(x.device):
+        gm = _meta_ptr(grad_meta, x.n, x.device, "grad_meta")
+        mm = _meta_ptr(exp_avg_meta, x.n, x.device, "exp_avg_meta")
+        if level == "O2":
+            _check(lib().msamp_quantize_adamw_o2_step(x.n, x.numel, x.ptrs, int(grad_fmt), gm, g.ptrs, m.ptrs,
+                                                      mm, v.ptrs, w.ptrs, ctypes.byref(hp), int(step),
+                                                      _stream(x.device)))
+        else:
+            _check(lib().msamp_quantize_adamw_o3_step(
+                x.n, x.numel, x.ptrs, int(grad_fmt), gm, g.ptrs, m.ptrs, mm, v.ptrs, w.ptrs, w8.ptrs,
+                _meta_ptr(weight_fp8_meta, x.n, x.device, "weight_fp8_meta"), ctypes.byref(hp), int(step),
+                _stream(x.device)))
+
+
 def step_constants(*, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int,
                    adam: bool = False) -> torch.Tensor:
     """The binary32 constants of one AdamW (adam=True: Adam) step as a CPU
@@ -518,6 +575,20 @@ def rmw_probe(grad, exp_avg, exp_avg_sq, weight) -> None:
         return
     with torch.cuda.device(g.device):
         _check(lib().msamp_rmw_probe(g.n, g.numel, g.ptrs, m.ptrs, v.ptrs, w.ptrs, _stream(g.device)))
+
+
+def stream_probe(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> None:
+    """Measurement aid: reads all of 'src' (dst None) or copies it into
+    'dst' (msamp_stream_probe); contiguous tensors of a multiple of 16 bytes."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous() or (dst is not None and not dst.is_contiguous()):
+        raise ValueError("stream_probe needs contiguous tensors")
+    if dst is not None and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    with torch.cuda.device(src.device):
+        _check(lib().msamp_stream_probe(0 if dst is None else 1, ctypes.c_void_p(src.data_ptr()),
+                                        ctypes.c_void_p(dst.data_ptr() if dst is not None else 0),
+                                        nbytes, _stream(src.device)))
 
 
 def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:

@@ -104,7 +104,9 @@ hipError_t timed(msamp_kernel_kind kind, hipStream_t s, F&& launch) {
 
 // ---------------------------------------------------------- plan cache ---
 
-enum PlanKind : uint64_t { kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3 };
+enum PlanKind : uint64_t {
+  kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3, kPlanQuantizeO2, kPlanQuantizeO3
+};
 
 // Device tables of one tensor list: amax scratch (two u32 per tensor, kept
 // at zero between calls), the descriptors and the chunk map, in one
@@ -185,7 +187,9 @@ void evict_locked(PlanCache& c) {
 }
 
 // Returns the plan of a tensor list, building and uploading it (on 'stream')
-// the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n);
+// the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n, or
+// null for a role the operation does not have): roles 0..4 fill p0..p4 of
+// the descriptors and role 5 fills aux;
 // 'min_one_chunk' gives every tensor at least one (possibly empty) chunk.
 // On success '*lease' holds the cache lock: the caller keeps it until its
 // launches are enqueued, so that no other thread can evict (and free) the
@@ -204,7 +208,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   key.push_back((uint64_t)n);
   for (int32_t t = 0; t < n; ++t) key.push_back((uint64_t)numel[t]);
   for (int r = 0; r < nroles; ++r)
-    for (int32_t t = 0; t < n; ++t) key.push_back((uint64_t)(uintptr_t)ptrs[r][t]);
+    for (int32_t t = 0; t < n; ++t) key.push_back(ptrs[r] ? (uint64_t)(uintptr_t)ptrs[r][t] : 0u);
   const uint64_t h = hash_words(key);
 
   PlanCache& c = cache();
@@ -264,13 +268,14 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     TensorDesc d;
     std::memset(&d, 0, sizeof d);
     d.numel = numel[t];
-    const void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    for (int r = 0; r < nroles && r < 5; ++r) p[r] = ptrs[r][t];
+    const void* p[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    for (int r = 0; r < nroles && r < 6; ++r) p[r] = ptrs[r] ? ptrs[r][t] : nullptr;
     d.p0 = p[0];
     d.p1 = const_cast<void*>(p[1]);
     d.p2 = const_cast<void*>(p[2]);
     d.p3 = const_cast<void*>(p[3]);
     d.p4 = const_cast<void*>(p[4]);
+    d.aux = p[5];
     hd[t] = d;
   }
   if (!chunks.empty())
@@ -458,6 +463,46 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   return MSAMP_OK;
 }
 
+// Gradient quantize + AdamW step (O2 or O3) with the quantize fused into
+// pass 1; the rest is the step's sequence.
+msamp_status quantize_step_impl(bool o3, int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                int grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
+                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_list(n, numel, (const void* const*)grad_f32, "grad_f32"));
+  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                             weight_fp8, weight_fp8_meta));
+  hipStream_t s = (hipStream_t)stream_ptr;
+  const void* const* roles[6] = {(const void* const*)grad,       (const void* const*)exp_avg,
+                                 (const void* const*)exp_avg_sq, (const void* const*)weight,
+                                 (const void* const*)weight_fp8, (const void* const*)grad_f32};
+  if (!o3) roles[4] = nullptr;
+  Plan* p = nullptr;
+  std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
+  MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, 6, false, s, &p, &lease));
+  const StepConsts k = make_consts(hp, step, false);
+  MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE_PASS1, s,
+               launch_quantize_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
+                                     p->scratch_a, k, s));
+  MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
+               launch_step_pass2(grad_fmt, o3, false, p->desc, p->chunks, p->nchunks, grad_meta,
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s));
+  if (o3)
+    MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+               launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
+                                    o3 ? weight_fp8_meta : nullptr, 448.0f, s));
+  return MSAMP_OK;
+}
+
 // Ablation: O2 AdamW step with a per-tensor-scaled FP16 second moment.
 msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* const* grad,
                                 int grad_fmt, const msamp_meta* grad_meta, uint8_t* const* exp_avg,
@@ -587,6 +632,7 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
   return MSAMP_OK;
 }
 
+
 }  // namespace
 }  // namespace msamp
 
@@ -611,6 +657,9 @@ const char* msamp_kernel_name(msamp_kernel_kind kind) {
     case MSAMP_KERNEL_AMAX_FINALIZE: return "amax_finalize";
     case MSAMP_KERNEL_O2_DELAYED: return "o2_delayed";
     case MSAMP_KERNEL_RMW_PROBE: return "rmw_probe";
+    case MSAMP_KERNEL_QUANTIZE_PASS1: return "quantize_pass1";
+    case MSAMP_KERNEL_READ_PROBE: return "read_probe";
+    case MSAMP_KERNEL_COPY_PROBE: return "copy_probe";
     default: return "";
   }
 }
@@ -872,6 +921,32 @@ msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const
   });
 }
 
+msamp_status msamp_quantize_adamw_o2_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                          msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                          uint8_t* const* grad, uint8_t* const* exp_avg,
+                                          msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                          uint16_t* const* weight, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream) {
+  return guarded([&]() {
+    return quantize_step_impl(false, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
+  });
+}
+
+msamp_status msamp_quantize_adamw_o3_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                          msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                          uint8_t* const* grad, uint8_t* const* exp_avg,
+                                          msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                          uint16_t* const* master, uint8_t* const* weight_fp8,
+                                          msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream) {
+  return guarded([&]() {
+    return quantize_step_impl(true, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step,
+                              stream);
+  });
+}
+
 msamp_status msamp_release_cache(void) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
@@ -888,6 +963,32 @@ msamp_status msamp_release_cache(void) {
     c.count = 0;
     c.bytes = 0;
     if (cur >= 0) (void)hipSetDevice(cur);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_stream_probe(msamp_stream_kind kind, const void* src, void* dst, int64_t bytes,
+                                void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    if (kind != MSAMP_STREAM_READ && kind != MSAMP_STREAM_COPY)
+      return fail(MSAMP_E_INVALID_ARG, "unknown stream probe kind");
+    if (bytes < 0 || bytes % 16 != 0) return fail(MSAMP_E_INVALID_ARG, "bytes must be >= 0 and a multiple of 16");
+    if (bytes == 0) return MSAMP_OK;
+    if (src == nullptr) return fail(MSAMP_E_INVALID_ARG, "src is NULL");
+    if (!aligned16(src)) return fail(MSAMP_E_MISALIGNED, "src is not 16-byte aligned");
+    const bool copy = kind == MSAMP_STREAM_COPY;
+    if (copy) {
+      if (dst == nullptr) return fail(MSAMP_E_INVALID_ARG, "dst is NULL");
+      if (!aligned16(dst)) return fail(MSAMP_E_MISALIGNED, "dst is not 16-byte aligned");
+      const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+      if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
+        return fail(MSAMP_E_INVALID_ARG, "src and dst overlap");
+    }
+    if (bytes / 16 / (16 * 1024) >= (int64_t)UINT32_MAX) return fail(MSAMP_E_INVALID_ARG, "bytes too large");
+    hipStream_t s = (hipStream_t)stream;
+    MSAMP_LAUNCH(copy ? MSAMP_KERNEL_COPY_PROBE : MSAMP_KERNEL_READ_PROBE, s,
+                 launch_stream_probe(copy, src, dst, bytes, s));
     return MSAMP_OK;
   });
 }

@@ -270,6 +270,66 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   block_max_into(mx, &amax_m[r.t]);
 }
 
+// Gradient quantize fused with pass 1 (AdamW, O2 and O3). The codes are
+// computed exactly as k_quantize computes them (same scale, same NaN-aware
+// saturating encode), stored, and decoded from registers for pass 1, so they
+// are not read back from memory. Every stream uses the FP32 lane layout
+// (4-element groups): 16-byte gradient loads, 4-byte code loads and stores.
+template <int GF>
+__global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __restrict__ desc,
+                                                           const ChunkRef* __restrict__ chunks,
+                                                           msamp_meta* __restrict__ gmeta,
+                                                           const msamp_meta* __restrict__ mmeta,
+                                                           uint32_t* __restrict__ amax_m, StepConsts k) {
+  const ChunkRange r = chunk_range(chunks, desc);
+  const float s = scale_rule(gmeta[r.t].amax, Fp8Traits<GF>::kMax);
+  const float gsi = 1.0f / s;
+  if (chunks[blockIdx.x].chunk == 0 && threadIdx.x == 0) {
+    gmeta[r.t].scale = s;
+    gmeta[r.t].scale_inv = gsi;
+    gmeta[r.t].reserved = 0.0f;
+  }
+  const float msi = mmeta[r.t].scale_inv;
+  const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].aux);
+  // p0 is the step's (read-only) gradient role; this kernel produces it
+  GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(const_cast<void*>(desc[r.t].p0));
+  const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  uint32_t mx = 0u;
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    if (group4_base(tile, 3) + 4 <= r.end) {
+      u32x4 v[4];
+      uint32_t mw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = load_stream<u32x4>(x + group4_base(tile, j));
+        mw[j] = load_stream<uint32_t>(mq + group4_base(tile, j));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float f[4] = {__uint_as_float(v[j].x) * s, __uint_as_float(v[j].y) * s,
+                            __uint_as_float(v[j].z) * s, __uint_as_float(v[j].w) * s};
+        const uint32_t c = enc4_nan<GF>(f);
+        store_stream<uint32_t>(q + group4_base(tile, j), c);
+        float g[4], m[4];
+        dec4<GF>(c, g);
+        dec4<kE4M3>(mw[j], m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = umax(mx, abs_bits(first_moment(k, g[i] * gsi, m[i] * msi)));
+      }
+    } else {
+      for (int j = 0; j < 4; ++j) {
+        const int64_t e = group4_base(tile, j);
+        for (int64_t i = e; i < e + 4 && i < r.end; ++i) {
+          const uint32_t c = enc1_nan<GF>(x[i] * s);
+          q[i] = (uint8_t)c;
+          mx = umax(mx, abs_bits(first_moment(k, dec1<GF>((uint8_t)c) * gsi, dec1<kE4M3>(mq[i]) * msi)));
+        }
+      }
+    }
+  }
+  block_max_into(mx, &amax_m[r.t]);
+}
+
 // Pass 2: recompute m1 exactly as in pass 1, then v1, w1; store m (E4M3 with
 // the new scale), v and w (FP16). In the O3 layout the weight is the master
 // and the amax of the stored master is reduced into amax_w.
@@ -627,6 +687,47 @@ __global__ __launch_bounds__(kBlock) void k_rmw_probe(const TensorDesc* __restri
   }
 }
 
+// Plain streams over one buffer in 16-byte units (measurement aid): the
+// lanes of the amax kernel's FP32 layout (each wave instruction covers 1 KB
+// of consecutive memory, 16 KB per tile, 256 KB per workgroup), non-temporal
+// loads and stores. READ only loads (the empty asm keeps the loaded values
+// live, so the loads are issued and waited for); COPY stores what it loads.
+constexpr int64_t kProbeTileUnits = 1024, kProbeChunkUnits = 16 * kProbeTileUnits;
+
+template <bool COPY>
+__global__ __launch_bounds__(kBlock) void k_stream_probe(const u32x4* __restrict__ src_p,
+                                                         u32x4* __restrict__ dst_p, int64_t units) {
+  const GLOBAL u32x4* __restrict__ src = (const GLOBAL u32x4*)src_p;
+  GLOBAL u32x4* __restrict__ dst = (GLOBAL u32x4*)dst_p;
+  const int64_t begin = (int64_t)blockIdx.x * kProbeChunkUnits;
+  const int64_t end = begin + kProbeChunkUnits < units ? begin + kProbeChunkUnits : units;
+  const int64_t lane = (threadIdx.x >> 6) * 256 + (threadIdx.x & 63);
+  for (int64_t tile = begin; tile < end; tile += kProbeTileUnits) {
+    if (tile + kProbeTileUnits <= end) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = load_stream<u32x4>(src + tile + lane + k * 64);
+      if (COPY) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) store_stream<u32x4>(dst + tile + lane + k * 64, v[k]);
+      } else {
+        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+      }
+    } else {
+      for (int k = 0; k < 4; ++k) {
+        const int64_t i = tile + lane + k * 64;
+        if (i < end) {
+          u32x4 x = src[i];
+          if (COPY)
+            dst[i] = x;
+          else
+            asm volatile("" ::"v"(x));
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void k_codec_probe(int op, const void* __restrict__ in,
                                                         void* __restrict__ out, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
@@ -708,6 +809,17 @@ static void pass1_launch(unsigned g, hipStream_t stream, const TensorDesc* desc,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
                          const StepConsts& k, const StepConsts* kdev) {
   k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+}
+
+hipError_t launch_quantize_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
+                                 msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                                 const StepConsts& k, hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  if (gfmt == kE4M3)
+    k_quantize_pass1<kE4M3><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+  else
+    k_quantize_pass1<kE5M2><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+  return hipGetLastError();
 }
 
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
@@ -847,6 +959,17 @@ hipError_t launch_meta_from_amax(int32_t n, const float* amax, msamp_meta* meta,
                                  hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   k_meta_from_amax<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(n, amax, meta, fmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_probe(bool copy, const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  const int64_t units = bytes / 16;
+  if (units <= 0) return hipSuccess;
+  const unsigned g = (unsigned)((units + kProbeChunkUnits - 1) / kProbeChunkUnits);
+  if (copy)
+    k_stream_probe<true><<<g, kBlock, 0, stream>>>((const u32x4*)src, (u32x4*)dst, units);
+  else
+    k_stream_probe<false><<<g, kBlock, 0, stream>>>((const u32x4*)src, (u32x4*)dst, units);
   return hipGetLastError();
 }
 

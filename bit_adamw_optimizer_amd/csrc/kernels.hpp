@@ -24,6 +24,8 @@ constexpr int64_t kChunk = 16 * kTile;  // 65536 elements
 //   dequantize    q u8          out f32       -            -           -
 //   O2 step       grad u8       exp_avg u8    exp_avg_sq   weight      -
 //   O3 step       grad u8       exp_avg u8    exp_avg_sq   master      weight_fp8
+// The quantizing steps use the step roles with p0 written by the fused
+// quantize + pass 1, and 'aux' holding the binary32 gradient it reads.
 struct TensorDesc {
   const void* p0;
   void* p1;
@@ -31,7 +33,8 @@ struct TensorDesc {
   void* p3;
   void* p4;
   int64_t numel;
-  int64_t reserved[2];
+  const void* aux;
+  int64_t reserved;
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor must stay 64 bytes");
 
@@ -64,6 +67,12 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
                              int64_t nchunks, const msamp_meta* meta, hipStream_t stream);
 // 'coupled' selects Adam (L2 term wd*w added to the gradient before the
 // moments); otherwise AdamW.
+// Fused gradient quantize + AdamW pass 1: q = enc(x * s) into p0 (s from
+// gmeta.amax; chunk 0 writes gmeta.scale / .scale_inv) and the pass-1 amax of
+// the new first moment from the codes in registers.
+hipError_t launch_quantize_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
+                                 msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                                 const StepConsts& k, hipStream_t stream);
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream,
@@ -101,6 +110,9 @@ hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64
 hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
                                 uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
                                 hipStream_t stream);
+// Measurement streams: read 'bytes' from src, or copy them to dst (bytes a
+// multiple of 16, 16-byte aligned pointers).
+hipError_t launch_stream_probe(bool copy, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_codec_probe(int op, const void* in, void* out, int64_t n, hipStream_t stream);
 // Split-phase steps: out[t] <- amax[t] as binary32 and amax[t] <- 0; and
 // meta[t] <- {a, scale(a, fmax), 1/scale, 0} from a caller's amax array.

@@ -219,6 +219,54 @@ def grad_tensor(w: Workload, t: int, step: int, device, out: Optional[torch.Tens
     return out
 
 
+def _storage_pieces(views: Sequence[torch.Tensor], piece: int):
+    """The one allocation behind 'views' (views of one buffer, in order), as
+    consecutive slices of at most 'piece' elements."""
+    base = views[0]
+    buf = torch.empty(0, dtype=base.dtype, device=base.device).set_(base.untyped_storage())
+    total = buf.numel()
+    return [buf[a:min(total, a + piece)] for a in range(0, total, piece)]
+
+
+def _flat_seed(w: Workload, role: int, step: int) -> int:
+    return ((w.seed_base * 1_000_003 + 999_983) * 1009 + step) * 7 + role
+
+
+def init_weights_flat(w: Workload, views: Sequence[torch.Tensor], device, piece: int = 1 << 28) -> None:
+    """FP16 weights of N(0, 0.02) drawn over the views' one allocation in a
+    few launches (one generator per list, not per tensor): the same
+    distribution as init_weights, for lists of many small tensors."""
+    g = _gen(device, _flat_seed(w, 0, 0))
+    for sl in _storage_pieces(views, piece):
+        x = torch.randn(sl.numel(), generator=g, device=device, dtype=torch.float32)
+        sl.copy_((x * 0.02).to(torch.float16))
+
+
+def grads_flat(w: Workload, step: int, views: Sequence[torch.Tensor], device, piece: int = 1 << 28) -> None:
+    """The binary32 gradients of a step drawn over the views' one allocation
+    in a few launches: the distribution of grad_tensor (normal or Student-t
+    with 3 degrees of freedom, times grad_sigma), zero on the all-zero
+    tensors. For lists without per-tensor factors."""
+    assert w.factor is None
+    g = _gen(device, _flat_seed(w, 1, step))
+    for sl in _storage_pieces(views, piece):
+        k = sl.numel()
+        torch.randn(k, generator=g, device=device, out=sl)
+        if w.grad_kind == "student_t3":
+            chi = torch.zeros(k, dtype=torch.float32, device=device)
+            tmp = torch.empty(k, dtype=torch.float32, device=device)
+            for _ in range(3):
+                torch.randn(k, generator=g, device=device, out=tmp)
+                chi.addcmul_(tmp, tmp)
+            sl.div_(torch.sqrt(chi / 3.0))
+            del chi, tmp
+        elif w.grad_kind != "normal":
+            raise ValueError(w.grad_kind)
+        sl.mul_(w.grad_sigma)
+    for t in w.zero_tensors:
+        views[t].zero_()
+
+
 def grads(w: Workload, step: int, device) -> List[torch.Tensor]:
     return [grad_tensor(w, t, step, device) for t in range(w.n)]
 

@@ -223,6 +223,39 @@ msamp_status msamp_adamw_o3_step(int32_t n, const int64_t* numel, const uint8_t*
                                  const msamp_adamw_hparams* hp, int64_t step, void* stream);
 
 /*
+ * msamp_quantize_adamw_o2_step / msamp_quantize_adamw_o3_step -- the
+ * gradient quantize (msamp_quantize_fp8) and the AdamW step
+ * (msamp_adamw_o2_step / msamp_adamw_o3_step) in one call, the quantize
+ * done in the same pass as the step's pass 1: each FP8 gradient code is
+ * computed once, stored to grad[t] and decoded from registers, so pass 1
+ * does not read the codes back ([TE]: every cast between formats costs a
+ * full pass over the tensor). Every output (codes, gradient scales, state,
+ * meta) is bit-identical to msamp_quantize_fp8 followed by the step.
+ *   grad_f32[t]  device binary32 gradient, read
+ *   grad_meta[t] device, in (.amax, e.g. from msamp_amax) / out (.scale,
+ *                .scale_inv, .reserved = 0), as msamp_quantize_fp8
+ *   grad[t]      device uint8, out: the gradient's FP8 codes in grad_fmt
+ *   other arguments, layouts and errors as msamp_adamw_o2_step /
+ *   msamp_adamw_o3_step.
+ * Passes: quantize + pass 1 (read g 4, m 1; write codes 1), pass 2 (11)
+ * [, pass 3 (3)]: 17 bytes per element (O2) or 20 (O3), against 18 / 21 for
+ * the two calls.
+ */
+msamp_status msamp_quantize_adamw_o2_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                          msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                          uint8_t* const* grad, uint8_t* const* exp_avg,
+                                          msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                          uint16_t* const* weight, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream);
+msamp_status msamp_quantize_adamw_o3_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                          msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                          uint8_t* const* grad, uint8_t* const* exp_avg,
+                                          msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                          uint16_t* const* master, uint8_t* const* weight_fp8,
+                                          msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp,
+                                          int64_t step, void* stream);
+
+/*
  * msamp_adam_o2_step / msamp_adam_o3_step -- the same steps for
  * torch.optim.Adam, the other optimizer the MS-AMP README recognizes ([RD]
  * "Usage"): weight decay is an L2 term added to the gradient before the
@@ -412,6 +445,21 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
                              uint8_t* const* exp_avg, uint16_t* const* exp_avg_sq,
                              uint16_t* const* weight, void* stream);
 
+/*
+ * msamp_stream_probe -- MEASUREMENT AID, not part of the method: a plain
+ * stream at the launch shape of the library's kernels (16-byte accesses,
+ * each wave instruction on 1 KB of consecutive memory, 256 KB per
+ * workgroup, non-temporal hints), giving the rates the memory system offers
+ * a pure read and a copy, beside msamp_rmw_probe's read-modify-write:
+ *   MSAMP_STREAM_READ  reads 'bytes' from src; dst is not used (may be NULL)
+ *   MSAMP_STREAM_COPY  copies 'bytes' from src to dst (no overlap)
+ * src, dst device, 16-byte aligned; bytes >= 0 and a multiple of 16. Invalid
+ * arguments return MSAMP_E_INVALID_ARG / MSAMP_E_MISALIGNED before any launch.
+ */
+typedef enum { MSAMP_STREAM_READ = 0, MSAMP_STREAM_COPY = 1 } msamp_stream_kind;
+msamp_status msamp_stream_probe(msamp_stream_kind kind, const void* src, void* dst, int64_t bytes,
+                                void* stream);
+
 /* Kernel timing with HIP events recorded on the launch stream around every
  * kernel the library enqueues (off by default). */
 typedef enum {
@@ -426,7 +474,10 @@ typedef enum {
   MSAMP_KERNEL_AMAX_FINALIZE = 8, /* amax write-back of msamp_amax */
   MSAMP_KERNEL_O2_DELAYED = 9,  /* one-pass delayed-scaling ablation */
   MSAMP_KERNEL_RMW_PROBE = 10,  /* msamp_rmw_probe (measurement aid) */
-  MSAMP_KERNEL_COUNT = 11
+  MSAMP_KERNEL_QUANTIZE_PASS1 = 11, /* gradient quantize fused with pass 1 */
+  MSAMP_KERNEL_READ_PROBE = 12, /* msamp_stream_probe, MSAMP_STREAM_READ */
+  MSAMP_KERNEL_COPY_PROBE = 13, /* msamp_stream_probe, MSAMP_STREAM_COPY */
+  MSAMP_KERNEL_COUNT = 14
 } msamp_kernel_kind;
 
 /* on != 0 starts recording (and discards earlier records; the events for

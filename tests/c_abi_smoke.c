@@ -48,6 +48,30 @@ int main(void) {
              MSAMP_E_INVALID_ARG, 11);
   EXPECT(strstr(msamp_last_error(), "beta2") != NULL, 12);
   EXPECT(strcmp(msamp_kernel_name(MSAMP_KERNEL_AMAX), "amax") == 0, 13);
+
+  /* the quantizing steps validate the binary32 gradient list too */
+  hp.beta2 = 0.999;
+  const float* xf[1] = {(const float*)(uintptr_t)0x700008};
+  uint8_t* gq[1] = {(uint8_t*)(uintptr_t)0x300000};
+  EXPECT(msamp_quantize_adamw_o2_step(1, numel, xf, MSAMP_FP8_E4M3, meta, gq, m, meta, v, w, &hp, 1, NULL) ==
+             MSAMP_E_MISALIGNED, 14);
+  EXPECT(strstr(msamp_last_error(), "grad_f32[0]") != NULL, 15);
+  xf[0] = (const float*)(uintptr_t)0x700000;
+  uint8_t* w8[1] = {NULL};
+  EXPECT(msamp_quantize_adamw_o3_step(1, numel, xf, MSAMP_FP8_E5M2, meta, gq, m, meta, v, w, w8, meta, &hp, 1,
+                                      NULL) == MSAMP_E_INVALID_ARG, 16);
+  EXPECT(strstr(msamp_last_error(), "weight_fp8[0]") != NULL, 17);
+
+  /* measurement streams: size, alignment and overlap checks */
+  void* src = (void*)(uintptr_t)0x800000;
+  void* dst = (void*)(uintptr_t)0x800100;
+  EXPECT(msamp_stream_probe(MSAMP_STREAM_READ, src, NULL, 24, NULL) == MSAMP_E_INVALID_ARG, 18);
+  EXPECT(msamp_stream_probe(MSAMP_STREAM_COPY, src, dst, 4096, NULL) == MSAMP_E_INVALID_ARG, 19);
+  EXPECT(strstr(msamp_last_error(), "overlap") != NULL, 20);
+  EXPECT(msamp_stream_probe(MSAMP_STREAM_COPY, src, (void*)(uintptr_t)0x900008, 16, NULL) == MSAMP_E_MISALIGNED,
+         21);
+  EXPECT(msamp_stream_probe((msamp_stream_kind)5, src, dst, 16, NULL) == MSAMP_E_INVALID_ARG, 22);
+  EXPECT(msamp_stream_probe(MSAMP_STREAM_READ, src, NULL, 0, NULL) == MSAMP_OK, 23);
   printf("c abi ok\n");
   return 0;
 }

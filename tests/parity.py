@@ -80,9 +80,10 @@ class GpuState:
     """Device state of one workload, driven through the C ABI."""
 
     def __init__(self, w: W.Workload, device, adam: bool = False, delayed: bool = False,
-                 scaled_v: bool = False, flat: bool = False):
+                 scaled_v: bool = False, flat: bool = False, fused: bool = False):
         self.w = w
         self.device = device
+        self.fused = fused  # gradient quantize fused with pass 1 (AdamW only)
         self.adam = adam  # Adam (coupled L2) instead of AdamW
         self.delayed = delayed  # one-pass delayed-scaling ablation (O2 AdamW)
         self.scaled_v = scaled_v  # scaled-FP16-v ablation (O2 AdamW)
@@ -119,6 +120,16 @@ class GpuState:
     def step(self, step: int) -> None:
         w = self.w
         M.amax(self.tl_g32, self.grad_meta)
+        if self.fused:
+            assert not (self.adam or self.delayed or self.scaled_v)
+            if w.level == "O2":
+                M.quantize_adamw_o2_step(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq, self.tl_m,
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
+            else:
+                M.quantize_adamw_o3_step(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq, self.tl_m,
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
+                                         self.weight_fp8_meta, step=step, **w.hparams())
+            return
         M.quantize_fp8(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq)
         if w.level == "O2" and self.scaled_v:
             M.adamw_o2_step_scaled_v(self.tl_gq, w.grad_fmt, self.grad_meta, self.tl_m,
@@ -146,13 +157,13 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def run_parity(w: W.Workload, steps: int, verify=None, threads: int = 16, device="cuda",
                adam: bool = False, delayed: bool = False, scaled_v: bool = False,
-               flat: bool = False):
+               flat: bool = False, fused: bool = False):
     """Runs 'steps' steps on the GPU and on the oracle (for the tensors in
     'verify', default all) and returns a dict of Stats per output. adam=True
     runs the Adam (coupled L2) entry points instead of AdamW."""
     verify = list(range(w.n)) if verify is None else list(verify)
     t0 = time.time()
-    gs = GpuState(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, flat=flat)
+    gs = GpuState(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, flat=flat, fused=fused)
     torch.cuda.synchronize()
     ost = {t: O.TensorState(host(gs.weights[t]), w.level, adam=adam, delayed=delayed,
                             scaled_v=scaled_v) for t in verify}

@@ -20,10 +20,6 @@ def _report(name, stats):
                                   for k, s in stats.items() if s.total))
 
 
-def _idx(w, names):
-    return [w.names.index(n) for n in names]
-
-
 def _code_invariant(gs, w, verify):
     # every tensor whose new first moment is nonzero fills the E4M3 range
     mm = gs.exp_avg_meta.cpu().numpy()
@@ -32,10 +28,19 @@ def _code_invariant(gs, w, verify):
             assert (host(gs.exp_avg[t]) & 0x7F).max() == 0x7E, w.names[t]
 
 
+def _first_last_layers(w, last):
+    """embed_tokens, lm_head, the final norm and every tensor of the first and
+    last decoder layers: every distinct tensor size of the list."""
+    keep = [t for t, nm in enumerate(w.names)
+            if nm in ("embed_tokens", "lm_head", "norm") or nm.startswith("layers.0.")
+            or nm.startswith("layers.%d." % last)]
+    assert set(w.numel[t] for t in keep) == set(w.numel)
+    return keep
+
+
 def test_llama2_7b_o2_5_steps():
     w = W.make("llama2_7b")
-    verify = _idx(w, ["layers.0.q_proj", "layers.31.down_proj", "layers.0.input_layernorm",
-                      "layers.31.post_attention_layernorm", "norm"])
+    verify = _first_last_layers(w, 31)
     log("llama2_7b O2: %d tensors, %d params; verifying %d tensors (%d params)"
         % (w.n, w.params, len(verify), sum(w.numel[t] for t in verify)))
     stats, gs, _ = run_parity(w, 5, verify=verify, flat=True)
@@ -48,7 +53,7 @@ def test_llama2_7b_o2_5_steps():
 
 def test_llama2_13b_o3_3_steps():
     w = W.make("llama2_13b")
-    verify = _idx(w, ["layers.0.k_proj", "layers.39.input_layernorm", "norm"])
+    verify = _first_last_layers(w, 39)
     log("llama2_13b O3: %d tensors, %d params; verifying %d tensors (%d params)"
         % (w.n, w.params, len(verify), sum(w.numel[t] for t in verify)))
     stats, gs, _ = run_parity(w, 3, verify=verify, flat=True)
@@ -139,4 +144,20 @@ def test_one_tensor_beyond_2_pow_32_elements():
         _report("2^32+ step %d" % s, stats)
     assert_bar(stats)
     del x, q, m, v, w
+    torch.cuda.empty_cache()
+
+
+def test_llama2_7b_fused_quantize_step_3_steps():
+    """The gradient quantize fused with pass 1 over the whole 7B list, one
+    tensor of every distinct size checked against the oracle."""
+    w = W.make("llama2_7b")
+    verify = [w.names.index(nm) for nm in ("embed_tokens", "layers.0.q_proj", "layers.0.gate_proj",
+                                            "layers.0.input_layernorm")]
+    assert set(w.numel[t] for t in verify) == set(w.numel)
+    log("llama2_7b O2 fused: verifying %d tensors (%d params)" % (len(verify), sum(w.numel[t] for t in verify)))
+    stats, gs, _ = run_parity(w, 3, verify=verify, flat=True, fused=True)
+    _report("llama2_7b fused", stats)
+    assert_bar(stats)
+    _code_invariant(gs, w, verify)
+    del gs
     torch.cuda.empty_cache()

@@ -1,0 +1,77 @@
+"""The gradient quantize fused with pass 1 of the AdamW step
+(msamp_quantize_adamw_o2_step / _o3_step) against the oracle's unfused
+sequence (quantize, then the step: MS-AMP "Optimization Level" page, sections
+O2 and O3), and byte for byte against the library's own two calls
+(msamp_quantize_fp8 then msamp_adamw_o2_step / _o3_step)."""
+import pytest
+import torch
+
+import bit_adamw_optimizer_amd as M
+from bit_adamw_optimizer_amd import workloads as W
+from tests.parity import GpuState, assert_bar, host, log, run_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, stats):
+    log("%s: " % name + ", ".join("%s %.6f/%dulp" % (k, s.frac, s.max_ulp)
+                                  for k, s in stats.items() if s.total))
+
+
+@pytest.mark.parametrize("wl", ["tiny_llama", "tiny_llama_o3", "tiny_stress"])
+def test_fused_quantize_step_matches_the_oracle(wl):
+    w = W.make(wl)
+    log("%s %s fused, %d tensors, %d params" % (wl, w.level, w.n, w.params))
+    stats, gs, _ = run_parity(w, 10 if wl != "tiny_stress" else 6, fused=True)
+    _report(wl + " fused", stats)
+    assert_bar(stats)
+    mm = gs.exp_avg_meta.cpu().numpy()
+    for t in w.zero_tensors:
+        assert (host(gs.exp_avg[t]) == 0).all()
+        assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
+
+
+def test_fused_ragged_sizes():
+    """Sizes around the 4-element group, the 4096-element tile and the
+    65536-element chunk, including empty tensors."""
+    sizes = [0, 1, 3, 4, 5, 15, 16, 17, 1023, 1024, 1025, 4095, 4096, 4097, 65535, 65536, 65537,
+             131072 + 4096 + 9, 0, 7]
+    for level, fmt in (("O2", W.E4M3), ("O3", W.E5M2)):
+        w = W.Workload("fused_ragged_%s_%d" % (level, fmt), level, fmt, 3, ["t%d" % i for i in range(len(sizes))],
+                       sizes, lr=5e-3, betas=(0.8, 0.99), eps=1e-7, weight_decay=0.05, seed_base=13)
+        stats, _, _ = run_parity(w, 3, fused=True)
+        _report(w.name, stats)
+        assert_bar(stats)
+
+
+def _snapshot(gs, level):
+    parts = gs.grad_q + [gs.grad_meta] + gs.exp_avg + [gs.exp_avg_meta] + gs.exp_avg_sq + gs.weights
+    if level == "O3":
+        parts += gs.weight_fp8 + [gs.weight_fp8_meta]
+    return [x.clone() for x in parts]
+
+
+@pytest.mark.parametrize("wl", ["tiny_stress", "tiny_llama_o3"])
+def test_fused_equals_quantize_then_step_byte_for_byte(wl):
+    """Every output of the fused call, gradient codes and scales included,
+    equals the two calls' outputs, step after step; step 3 plants NaN, +Inf
+    and -Inf in one tensor's gradient (the codes and scales of a non-finite
+    gradient are defined; the step of that tensor is outside the contract,
+    but both paths run the same arithmetic on it)."""
+    w = W.make(wl)
+    ref = GpuState(w, "cuda")
+    fus = GpuState(w, "cuda", fused=True)
+    big = max(range(w.n), key=lambda t: w.numel[t])
+    for s in range(1, 5):
+        for gs in (ref, fus):
+            gs.fill_grads(s)
+            if s == 3:
+                gs.grad_f32[big][5] = float("nan")
+                gs.grad_f32[big][6] = float("inf")
+                gs.grad_f32[big][7] = -float("inf")
+            gs.step(s)
+        torch.cuda.synchronize()
+        a, b = _snapshot(ref, w.level), _snapshot(fus, w.level)
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (wl, s, i)
+    log("%s: fused and two-call paths identical over 4 steps" % wl)
