@@ -1,7 +1,7 @@
 """bench.py end to end on a small parameter list (GPT-2-small shapes), in a
 child process: one JSON line with every key of the benchmark contract, a
-roofline record for the dominant kernel with its same-buffers ceiling, and
-the same in HIP-graph replay mode."""
+roofline record for the dominant kernel with its same-buffers ceilings, the
+fused and two-call gradient quantize, and the HIP-graph replay mode."""
 import json
 import os
 import subprocess
@@ -41,6 +41,17 @@ def test_bench_json_contract():
     assert rf["kernel"] == "o2_pass2" and 0 < rf["frac"] < 1
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert 0 < rf["same_buffers_ceiling"]["frac"] < 1.2
+    assert set(rf["ceilings"]) == {"read", "copy", "update_pass_mix"}
+    assert all(c["GB/s"] > 0 for c in rf["ceilings"].values())
+    # default: the gradient quantize runs fused with pass 1 (21 bytes per parameter)
+    assert d["config"]["fused_quantize"] is True and d["bytes_per_param"] == 21
+    assert set(d["kernels"]) >= {"amax", "quantize_pass1", "o2_pass2", "finalize"}
+    assert d["optimizer_step"]["includes_grad_quantize"] is True
+
+
+def test_bench_separate_quantize():
+    d = _run("--separate-quantize")
+    assert d["config"]["fused_quantize"] is False and d["bytes_per_param"] == 22
     assert set(d["kernels"]) >= {"amax", "quantize_fp8", "step_pass1", "o2_pass2"}
 
 
