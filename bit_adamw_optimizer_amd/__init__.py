@@ -34,7 +34,7 @@ __all__ = [
     # steps
     "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
     "step_constants", "adamw_o2_step_devconst", "adamw_o3_step_devconst", "adamw_step_phase",
-    "quantize_adamw_o2_step", "quantize_adamw_o3_step",
+    "adamw_o2_step_noalloc", "quantize_adamw_o2_step", "quantize_adamw_o3_step",
     # ablations
     "adamw_o2_step_delayed", "adamw_o2_step_scaled_v",
     # state helpers
@@ -123,6 +123,8 @@ def lib():
         L.msamp_quantize_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                                    vp, ctypes.POINTER(_HParams), i64, vp]
         L.msamp_quantize_adamw_o3_step.restype = st
+        L.msamp_adamw_o2_step_noalloc.argtypes = L.msamp_adamw_o2_step.argtypes
+        L.msamp_adamw_o2_step_noalloc.restype = st
         L.msamp_adam_o2_step.argtypes = L.msamp_adamw_o2_step.argtypes
         L.msamp_adam_o2_step.restype = st
         L.msamp_adam_o3_step.argtypes = L.msamp_adamw_o3_step.argtypes
@@ -519,6 +521,13 @@ def adamw_step_phase(phase: int, level: str, grad, grad_fmt: int, grad_meta, exp
     entry = "msamp_adamw_%s_step_phase%d" % (level.lower(), phase)
     with torch.cuda.device(dev):
         _check(getattr(lib(), entry)(*args, _stream(dev)))
+
+
+def adamw_o2_step_noalloc(*args, **kw) -> None:
+    """msamp_adamw_o2_step_noalloc: the O2 AdamW step with its tables in the
+    library's static device array (no allocation in the call); same arguments
+    as adamw_o2_step."""
+    adamw_o2_step(*args, _entry="msamp_adamw_o2_step_noalloc", **kw)
 
 
 def adam_o2_step(*args, **kw) -> None:

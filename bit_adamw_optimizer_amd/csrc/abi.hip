@@ -633,10 +633,164 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
 }
 
 
+// ------------------------------------------------- allocation-free step ---
+
+// Size of the static device array of msamp_adamw_o2_step_noalloc: enough
+// for the tables of 13.1e9 parameters in 291 tensors or 4.3e9 in 20,064.
+constexpr size_t kNoAllocScratchBytes = MSAMP_NOALLOC_SCRATCH_BYTES;
+// Devices whose scratch address the library keeps.
+constexpr int kNoAllocMaxDevices = 64;
+
+// Tables of msamp_adamw_o2_step_noalloc, rebuilt on every call in the
+// library's static device array (see 'scratch' below): two u32 amax words
+// per tensor (zero when the kernels start), the descriptor table and the
+// chunk map, each section 256-byte aligned.
+struct NoAllocLayout {
+  size_t scratch_bytes = 0, desc_bytes = 0, chunk_bytes = 0, total = 0;
+  int64_t nchunks = 0;
+};
+
+msamp_status noalloc_layout(int32_t n, const int64_t* numel, NoAllocLayout* l) {
+  int64_t chunks = 0;
+  for (int32_t t = 0; t < n; ++t) chunks += (numel[t] + kChunk - 1) / kChunk;
+  l->nchunks = chunks;
+  l->scratch_bytes = align_up(sizeof(uint32_t) * 2 * (size_t)n, 256);
+  l->desc_bytes = align_up(sizeof(TensorDesc) * (size_t)n, 256);
+  l->chunk_bytes = sizeof(ChunkRef) * (size_t)chunks;
+  l->total = l->scratch_bytes + l->desc_bytes + l->chunk_bytes;
+  if (l->total > kNoAllocScratchBytes)
+    return fail(MSAMP_E_INVALID_ARG,
+                "the tensor list needs " + std::to_string(l->total) + " bytes of tables (" +
+                    std::to_string(n) + " tensors, " + std::to_string(chunks) +
+                    " chunks of 65536 elements); msamp_adamw_o2_step_noalloc holds at most " +
+                    std::to_string(kNoAllocScratchBytes));
+  return MSAMP_OK;
+}
+
+// Host image of the tables, one for the whole process: the call holds
+// 'mu' from building it until the synchronous copy has read it.
+struct NoAllocHost {
+  std::mutex mu;
+  alignas(256) char image[kNoAllocScratchBytes];
+};
+
+NoAllocHost& noalloc_host() {
+  static NoAllocHost h;  // static storage: nothing is allocated at run time
+  return h;
+}
+
 }  // namespace
 }  // namespace msamp
 
 using namespace msamp;
+
+// The static device array of the allocation-free O2 step. In host code
+// 'scratch' names a host-side stand-in, not device memory: its device
+// address is taken once per device with hipGetSymbolAddress (each device has
+// its own copy) and only that address is passed to kernels and copies.
+static __device__ __align__(256) uint8_t scratch[msamp::kNoAllocScratchBytes];
+
+namespace {
+
+struct NoAllocDevices {
+  std::mutex mu;
+  void* ptr[kNoAllocMaxDevices] = {};  // device address of 'scratch', per device (null = not yet taken)
+};
+
+NoAllocDevices& noalloc_devices() {
+  static NoAllocDevices d;
+  return d;
+}
+
+// The device address of 'scratch' on device 'dev' (the current device).
+msamp_status noalloc_scratch(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(MSAMP_E_INVALID_ARG, "msamp_adamw_o2_step_noalloc supports devices 0..63");
+  NoAllocDevices& d = noalloc_devices();
+  std::lock_guard<std::mutex> lk(d.mu);
+  if (d.ptr[dev] != nullptr) {
+    *out = (uint8_t*)d.ptr[dev];
+    return MSAMP_OK;
+  }
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress of the step's static scratch");
+  if (ptr == nullptr) return fail(MSAMP_E_HIP, "hipGetSymbolAddress returned a null scratch address");
+  d.ptr[dev] = ptr;
+  *out = (uint8_t*)ptr;
+  return MSAMP_OK;
+}
+
+msamp_status step_noalloc_impl(int32_t n, const int64_t* numel, const uint8_t* const* grad, int grad_fmt,
+                               const msamp_meta* grad_meta, uint8_t* const* exp_avg,
+                               msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                               uint16_t* const* weight, const msamp_adamw_hparams* hp, int64_t step,
+                               void* stream_ptr) {
+  g_last_error.clear();
+  MSAMP_TRY(check_common(n, numel));
+  if (n == 0) return MSAMP_OK;
+  MSAMP_TRY(check_fmt(grad_fmt));
+  MSAMP_TRY(check_hparams(hp, step));
+  MSAMP_TRY(check_step_lists(false, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                             nullptr, nullptr));
+  NoAllocLayout l;
+  MSAMP_TRY(noalloc_layout(n, numel, &l));
+
+  hipStream_t s = (hipStream_t)stream_ptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(MSAMP_E_INVALID_ARG,
+                "msamp_adamw_o2_step_noalloc copies its tables from host memory at call time and "
+                "cannot be captured into a graph");
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  uint8_t* base = nullptr;
+  MSAMP_TRY(noalloc_scratch(dev, &base));
+
+  NoAllocHost& h = noalloc_host();
+  std::lock_guard<std::mutex> lk(h.mu);
+  char* hb = h.image;
+  std::memset(hb, 0, l.scratch_bytes + l.desc_bytes);  // amax words start at zero
+  TensorDesc* hd = (TensorDesc*)(hb + l.scratch_bytes);
+  for (int32_t t = 0; t < n; ++t) {
+    TensorDesc d;
+    std::memset(&d, 0, sizeof d);
+    d.numel = numel[t];
+    d.p0 = grad[t];
+    d.p1 = exp_avg[t];
+    d.p2 = exp_avg_sq[t];
+    d.p3 = weight[t];
+    hd[t] = d;
+  }
+  ChunkRef* hc = (ChunkRef*)(hb + l.scratch_bytes + l.desc_bytes);
+  for (int32_t t = 0, i = 0; t < n; ++t)
+    for (int64_t j = 0, k = (numel[t] + kChunk - 1) / kChunk; j < k; ++j) hc[i++] = {t, (int32_t)j};
+  // From pageable host memory the copy is synchronous: when it returns, the
+  // earlier work on the stream has finished and the image has been read.
+  e = hipMemcpyAsync(base, hb, l.total, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return fail_hip(e, "copy of the step tables into the static scratch");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "copy of the step tables into the static scratch");
+
+  uint32_t* amax_a = (uint32_t*)base;
+  uint32_t* amax_b = amax_a + n;
+  const TensorDesc* desc = (const TensorDesc*)(base + l.scratch_bytes);
+  const ChunkRef* chunks = (const ChunkRef*)(base + l.scratch_bytes + l.desc_bytes);
+  const StepConsts k = make_consts(hp, step, false);
+  MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
+               launch_step_pass1(grad_fmt, false, desc, chunks, l.nchunks, grad_meta, exp_avg_meta, amax_a, k, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_O2_PASS2, s,
+               launch_step_pass2(grad_fmt, false, false, desc, chunks, l.nchunks, grad_meta, exp_avg_meta, amax_a,
+                                 amax_b, k, s));
+  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+               launch_step_finalize(n, amax_a, exp_avg_meta, nullptr, nullptr, 448.0f, s));
+  return MSAMP_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -918,6 +1072,17 @@ msamp_status msamp_adamw_o2_step_scaled_v(int32_t n, const int64_t* numel, const
   return guarded([&]() {
     return step_scaled_v_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta,
                               exp_avg_sq, exp_avg_sq_meta, weight, hp, step, stream);
+  });
+}
+
+msamp_status msamp_adamw_o2_step_noalloc(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                         msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return step_noalloc_impl(n, numel, grad, (int)grad_fmt, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
+                             weight, hp, step, stream);
   });
 }
 

@@ -205,6 +205,34 @@ msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t*
                                  const msamp_adamw_hparams* hp, int64_t step, void* stream);
 
 /*
+ * msamp_adamw_o2_step_noalloc -- msamp_adamw_o2_step for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, bit-identical results, and no allocation of
+ * any kind in the call. Its tables (two u32 amax words per tensor, the
+ * 64-byte descriptor of each tensor, 8 bytes per 65,536-element chunk) live
+ * in a static device array of 4 MiB (MSAMP_NOALLOC_SCRATCH_BYTES) that each
+ * device holds from its first call until the process ends. They are rebuilt
+ * and copied into it on every call, synchronously: the call returns once
+ * the earlier work on the stream has finished and the copy is done, then
+ * the kernels run asynchronously as usual.
+ * Limit: round256(8 n) + round256(64 n) + 8 * sum_t ceil(numel[t] / 65536)
+ * <= MSAMP_NOALLOC_SCRATCH_BYTES (the Llama-2-13B list, 363 tensors and
+ * 13.0e9 parameters, needs 1.6 MB); a larger list returns
+ * MSAMP_E_INVALID_ARG before any device work.
+ * Every call on a device uses that device's one array and leaves the amax
+ * words at zero: calls that may overlap on one device (different streams or
+ * threads with no ordering between them) race and give undefined results.
+ * A stream being captured into a graph is rejected (MSAMP_E_INVALID_ARG).
+ * Arguments, layouts and other errors as msamp_adamw_o2_step.
+ */
+#define MSAMP_NOALLOC_SCRATCH_BYTES (4u << 20)
+msamp_status msamp_adamw_o2_step_noalloc(int32_t n, const int64_t* numel, const uint8_t* const* grad,
+                                         msamp_fp8_format grad_fmt, const msamp_meta* grad_meta,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
+/*
  * msamp_adamw_o3_step -- one AdamW step in the O3 layout ([OL] section O3
  * and table row "MS-AMP O3": FP16 master weight, FP8 regular weight), in
  * place. Arguments as msamp_adamw_o2_step, with the FP16 weight replaced by

@@ -72,6 +72,13 @@ int main(void) {
          21);
   EXPECT(msamp_stream_probe((msamp_stream_kind)5, src, dst, 16, NULL) == MSAMP_E_INVALID_ARG, 22);
   EXPECT(msamp_stream_probe(MSAMP_STREAM_READ, src, NULL, 0, NULL) == MSAMP_OK, 23);
+
+  /* the allocation-free step refuses a list whose tables exceed its static
+   * array, before any device work */
+  int64_t huge[1] = {(int64_t)1 << 35};
+  EXPECT(msamp_adamw_o2_step_noalloc(1, huge, g, MSAMP_FP8_E4M3, meta, m, meta, v, w, &hp, 1, NULL) ==
+             MSAMP_E_INVALID_ARG, 24);
+  EXPECT(strstr(msamp_last_error(), "at most") != NULL, 25);
   printf("c abi ok\n");
   return 0;
 }

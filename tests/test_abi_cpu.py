@@ -206,3 +206,27 @@ def test_binding_declares_the_signature_of_every_header_function():
         n_decl = 0 if args.strip() in ("", "void") else args.count(",") + 1
         assert len(fn.argtypes) == n_decl, (name, len(fn.argtypes), n_decl)
         assert fn.restype is not None, name
+
+
+def test_noalloc_step_rejects_lists_beyond_its_static_tables():
+    """The allocation-free step checks its table size before any device work:
+    one tensor of 2^35 elements needs 524,288 chunks (4 MiB of chunk map
+    plus the descriptor and amax sections), one byte past the limit."""
+    L = M.lib()
+    limit = 4 << 20
+
+    def call(numel):
+        st = L.msamp_adamw_o2_step_noalloc(1, _i64(numel), _vp(0x100000), 0, ctypes.c_void_p(0x10000),
+                                           _vp(0x200000), ctypes.c_void_p(0x20000), _vp(0x300000),
+                                           _vp(0x400000), ctypes.byref(GOOD_HP), 1, None)
+        return st, L.msamp_last_error().decode()
+
+    st, msg = call(1 << 35)
+    need = 256 + 256 + 8 * ((1 << 35) // 65536)
+    assert need > limit
+    assert st == 1 and "at most %d" % limit in msg and str(need) in msg, msg
+    # validation still comes first
+    st, msg = L.msamp_adamw_o2_step_noalloc(1, _i64(32), _vp(0), 0, ctypes.c_void_p(0x10000), _vp(0x200000),
+                                            ctypes.c_void_p(0x20000), _vp(0x300000), _vp(0x400000),
+                                            ctypes.byref(GOOD_HP), 1, None), L.msamp_last_error().decode()
+    assert st == 1 and "grad[0]" in msg
