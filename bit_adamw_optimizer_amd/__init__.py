@@ -41,6 +41,7 @@ __all__ = [
     "new_meta", "allocate_state", "flat_views", "state_bytes_per_param",
     # measurement and test aids
     "rmw_probe", "stream_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
+    "unpin_captured_tables", "cache_stats",
 ]
 
 E4M3 = 0
@@ -159,6 +160,10 @@ def lib():
         L.msamp_adamw_o3_step_devconst.restype = st
         L.msamp_release_cache.argtypes = []
         L.msamp_release_cache.restype = st
+        L.msamp_unpin_captured_tables.argtypes = []
+        L.msamp_unpin_captured_tables.restype = st
+        L.msamp_cache_stats.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.msamp_cache_stats.restype = st
         L.msamp_codec_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
         L.msamp_codec_probe.restype = st
         L.msamp_profile_enable.argtypes = [ctypes.c_int]
@@ -614,6 +619,19 @@ def codec_probe(op: int, inp: torch.Tensor, out: torch.Tensor) -> None:
 
 def release_cache() -> None:
     _check(lib().msamp_release_cache())
+
+
+def unpin_captured_tables() -> None:
+    """msamp_unpin_captured_tables: call after destroying graphs that
+    captured library calls."""
+    _check(lib().msamp_unpin_captured_tables())
+
+
+def cache_stats() -> dict:
+    """Cached tensor-list tables: {"lists", "bytes", "pinned"}."""
+    a, b, c = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().msamp_cache_stats(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return {"lists": a.value, "bytes": b.value, "pinned": c.value}
 
 
 def profile_enable(on: bool) -> None:

@@ -123,6 +123,9 @@ struct Plan {
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
   uint64_t last_use = 0;
+  // Used by a launch captured into a graph: its memory stays until
+  // msamp_unpin_captured_tables(), since a replay reads and writes it.
+  bool pinned = false;
 
   ~Plan() {
     if (dev) (void)hipFree(dev);
@@ -159,15 +162,16 @@ uint64_t hash_words(const std::vector<uint64_t>& w) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Evicts least recently used plans until the cache is within bounds, never
-// the most recently used one (it is being returned to a caller). Waits for
-// the device first: an evicted table may still be read by queued work.
+// the most recently used one (it is being returned to a caller) and never a
+// pinned one. Waits for the device first: an evicted table may still be read
+// by queued work.
 void evict_locked(PlanCache& c) {
   while (c.count > kMaxPlans || c.bytes > kMaxPlanBytes) {
     uint64_t best_tick = UINT64_MAX, best_hash = 0;
     size_t best_idx = 0;
     for (auto& kv : c.map)
       for (size_t i = 0; i < kv.second.size(); ++i)
-        if (kv.second[i]->last_use < best_tick && kv.second[i]->last_use != c.tick) {
+        if (kv.second[i]->last_use < best_tick && kv.second[i]->last_use != c.tick && !kv.second[i]->pinned) {
           best_tick = kv.second[i]->last_use;
           best_hash = kv.first;
           best_idx = i;
@@ -211,6 +215,14 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     for (int32_t t = 0; t < n; ++t) key.push_back(ptrs[r] ? (uint64_t)(uintptr_t)ptrs[r][t] : 0u);
   const uint64_t h = hash_words(key);
 
+  // A launch being captured into a graph keeps the plan's addresses: pin it.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    capture = hipStreamCaptureStatusNone;
+  }
+  const bool capturing = capture != hipStreamCaptureStatusNone;
+
   PlanCache& c = cache();
   std::unique_lock<std::mutex> lk(c.mu);
   auto it = c.map.find(h);
@@ -218,6 +230,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     for (auto& p : it->second)
       if (p->key == key) {
         p->last_use = ++c.tick;
+        if (capturing) p->pinned = true;
         *out = p.get();
         *lease = std::move(lk);
         return MSAMP_OK;
@@ -292,6 +305,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   if (e != hipSuccess) return fail_hip(e, "upload of the descriptor tables");
 
   plan->last_use = ++c.tick;
+  plan->pinned = capturing;
   *out = plan.get();
   c.bytes += plan->bytes;
   c.count += 1;
@@ -1120,14 +1134,50 @@ msamp_status msamp_release_cache(void) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     for (auto& kv : c.map)
-      for (auto& p : kv.second) {
-        (void)hipSetDevice(p->device);
-        (void)hipDeviceSynchronize();
-      }
-    c.map.clear();
-    c.count = 0;
-    c.bytes = 0;
+      for (auto& p : kv.second)
+        if (!p->pinned) {
+          (void)hipSetDevice(p->device);
+          (void)hipDeviceSynchronize();
+        }
+    for (auto it = c.map.begin(); it != c.map.end();) {
+      auto& vec = it->second;
+      for (size_t i = vec.size(); i-- > 0;)
+        if (!vec[i]->pinned) {
+          c.bytes -= vec[i]->bytes;
+          c.count -= 1;
+          vec.erase(vec.begin() + (ptrdiff_t)i);
+        }
+      it = vec.empty() ? c.map.erase(it) : std::next(it);
+    }
     if (cur >= 0) (void)hipSetDevice(cur);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_unpin_captured_tables(void) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    PlanCache& c = cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (auto& kv : c.map)
+      for (auto& p : kv.second) p->pinned = false;
+    ++c.tick;  // no plan is exempt from the eviction below as the newest
+    evict_locked(c);
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_cache_stats(int64_t* lists, int64_t* bytes, int64_t* pinned) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    PlanCache& c = cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    int64_t np = 0;
+    for (auto& kv : c.map)
+      for (auto& p : kv.second) np += p->pinned ? 1 : 0;
+    if (lists) *lists = (int64_t)c.count;
+    if (bytes) *bytes = (int64_t)c.bytes;
+    if (pinned) *pinned = np;
     return MSAMP_OK;
   });
 }

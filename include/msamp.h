@@ -64,6 +64,13 @@
  *     a list builds its tables (device and pinned host allocations, one
  *     upload on the stream); at most 64 lists (512 MB of tables) are kept,
  *     and evicting the least recently used one first waits for its device.
+ *   - Graph capture: a call whose stream is being captured uses the tables
+ *     built by an earlier eager call on the same lists (building them
+ *     allocates, which capture forbids) and PINS them: the captured kernels
+ *     keep their addresses, so pinned tables are neither evicted nor freed
+ *     by msamp_release_cache() (the cache may then exceed its bounds) until
+ *     msamp_unpin_captured_tables() is called, after the graphs that use
+ *     them have been destroyed or will not be replayed again.
  *   - Calls that use the same tensor lists must be ordered (same stream, or
  *     synchronized): they share that list's amax scratch.
  *   - Entry points may be called from several host threads at once; they
@@ -430,10 +437,19 @@ msamp_status msamp_adamw_o3_step_phase3(int32_t n, const int64_t* numel, const u
                                         uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                         const float* amax_w, void* stream);
 
-/* Frees every cached device table of the library (all devices) after
- * waiting for the devices to finish. Safe to call at any time from one
- * thread while no other library call runs. */
+/* Frees every cached device table of the library (all devices) that is not
+ * pinned by a graph capture, after waiting for the devices to finish. Safe to
+ * call at any time from one thread while no other library call runs. */
 msamp_status msamp_release_cache(void);
+
+/* Unpins every table pinned by a graph capture (see "Graph capture" above);
+ * call it once the graphs that use them are destroyed. The tables are then
+ * evicted or released like any other. */
+msamp_status msamp_unpin_captured_tables(void);
+
+/* Cached tables: number of tensor lists, their device bytes, and how many of
+ * them a graph capture pinned (each output may be NULL). */
+msamp_status msamp_cache_stats(int64_t* lists, int64_t* bytes, int64_t* pinned);
 
 /* ----------------------------------------------------------------------
  * Test- and measurement-facing entry points.

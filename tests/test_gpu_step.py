@@ -301,6 +301,61 @@ def test_graph_captured_step_replays_later_steps_bit_exact(level, adam, wl):
             assert torch.equal(a, b), "step %d differs" % s
 
 
+def test_captured_tables_survive_eviction_and_release_until_unpinned():
+    """The tables a captured graph uses are pinned: pushing 80 other lists
+    through the cache (past its 64-list bound) and calling
+    msamp_release_cache() frees every other table but not those, and the
+    graph still replays the exact eager trajectory. Unpinning lets
+    release_cache free them."""
+    w = W.make("tiny_llama")
+    ref = GpuState(w, "cuda")
+    gr = GpuState(w, "cuda")
+    consts = torch.empty(9, dtype=torch.float32, device="cuda")
+
+    def graph_step():
+        M.amax(gr.tl_g32, gr.grad_meta)
+        M.quantize_fp8(gr.tl_g32, w.grad_fmt, gr.grad_meta, gr.tl_gq)
+        M.adamw_o2_step_devconst(gr.tl_gq, w.grad_fmt, gr.grad_meta, gr.tl_m, gr.exp_avg_meta, gr.tl_v,
+                                 gr.tl_w, consts)
+
+    pinned0 = M.cache_stats()["pinned"]
+    graph = None
+    for s in range(1, 5):
+        ref.fill_grads(s)
+        ref.step(s)
+        gr.fill_grads(s)
+        consts.copy_(M.step_constants(step=s, **w.hparams()))
+        if s == 1:
+            graph_step()  # eager: builds the three tables
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                graph_step()
+            torch.cuda.synchronize()
+            st = M.cache_stats()
+            assert st["pinned"] == pinned0 + 3, st
+            # 80 other lists, then a release: only pinned tables remain
+            meta = M.new_meta(1, "cuda")
+            for i in range(80):
+                M.amax([torch.ones(64 + 16 * i, device="cuda")], meta)
+            torch.cuda.synchronize()
+            assert M.cache_stats()["lists"] <= 64 + st["pinned"]
+            M.release_cache()
+            st2 = M.cache_stats()
+            assert st2["pinned"] == st["pinned"] and st2["lists"] == st["pinned"], st2
+        else:
+            graph.replay()
+        torch.cuda.synchronize()
+        parts_r = ref.exp_avg + ref.exp_avg_sq + ref.weights + [ref.exp_avg_meta, ref.grad_meta]
+        parts_g = gr.exp_avg + gr.exp_avg_sq + gr.weights + [gr.exp_avg_meta, gr.grad_meta]
+        for a, b in zip(parts_r, parts_g):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "step %d differs" % s
+    del graph
+    M.unpin_captured_tables()
+    M.release_cache()
+    assert M.cache_stats() == {"lists": 0, "bytes": 0, "pinned": 0}
+
+
 @pytest.mark.parametrize("hp", [
     dict(lr=0.0, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),
     dict(lr=1e-2, betas=(0.0, 0.999), eps=1e-8, weight_decay=0.01),
