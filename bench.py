@@ -247,48 +247,62 @@ def numerics_report(st) -> dict:
     """Value statistics of the stored state after the timed steps: fractions
     of the FP16 second moment that are +-0 or subnormal (binary16 underflows
     (1-b2)*g^2 at small gradient scales) and of first-moment codes at 0 and
-    at +-max (0x7E)."""
-    import torch
-
-    n = zero = sub = 0
-    m_zero = m_max = 0
-    for v in st.tl_v.tensors:
-        b = v.view(torch.int16)
-        mag = b & 0x7FFF
-        n += b.numel()
-        zero += int((mag == 0).sum())
-        sub += int(((mag > 0) & (mag < 0x0400)).sum())
-    for m in st.tl_m.tensors:
-        mag = m & 0x7F
-        m_zero += int((mag == 0).sum())
-        m_max += int((mag == 0x7E).sum())
+    at +-max (0x7E). Counted over each role's one allocation in a few
+    launches; the alignment padding between tensors holds zeros that no
+    kernel writes, and is subtracted."""
+    n = sum(int(x.numel()) for x in st.tl_v.tensors)
+    v = storage_of(st.tl_v.tensors)
+    m = storage_of(st.tl_m.tensors)
+    pad_v, pad_m = v.numel() - n, m.numel() - n
+    vmag = v.view(torch_int16()) & 0x7FFF
+    zero = int((vmag == 0).sum()) - pad_v
+    sub = int(((vmag > 0) & (vmag < 0x0400)).sum())
+    mmag = m & 0x7F
+    m_zero = int((mmag == 0).sum()) - pad_m
+    m_max = int((mmag == 0x7E).sum())
     return {"v_zero_frac": zero / n, "v_subnormal_frac": sub / n,
             "m_code_zero_frac": m_zero / n, "m_code_max_frac": m_max / n}
 
 
+def torch_int16():
+    import torch
+
+    return torch.int16
+
+
 def cpu_baseline(w, device, threads: int) -> dict:
-    """The oracle on a bounded sample of the workload: the tensors of the
-    first four layers (one full step each: gradient amax + quantize + the
-    O2/O3 step), one thread per tensor (about 10 s on 16 host threads)."""
+    """The oracle on a bounded sample of the workload, one whole tensor per
+    work item (the per-tensor amax couples every element of a tensor, so a
+    tensor is the oracle's unit of work). For the Llama lists the sample is
+    chosen so that the threads get equal work: 'threads' MLP tensors and
+    twice as many attention projections (one MLP tensor and two projections
+    per thread, largest first), about 8 s on 16 host threads. Other lists
+    take their largest tensors, at most two per thread."""
     import numpy as np
     import torch
 
     import oracle as O
     from bit_adamw_optimizer_amd import workloads as W
 
-    idx = [t for t, nm in enumerate(w.names) if nm.split(".")[:2] in (["layers", "0"], ["layers", "1"],
-                                                                     ["layers", "2"], ["layers", "3"])]
-    if not idx:
-        idx = sorted(range(w.n), key=lambda t: -w.numel[t])[:8]
+    nthreads = max(1, threads)
+    mlp = [t for t, nm in enumerate(w.names) if nm.endswith(("gate_proj", "up_proj", "down_proj"))]
+    attn = [t for t, nm in enumerate(w.names) if nm.endswith(("q_proj", "k_proj", "v_proj", "o_proj"))]
+    if len(mlp) >= nthreads and len(attn) >= 2 * nthreads:
+        idx = mlp[:nthreads] + attn[:2 * nthreads]
+        how = "%d MLP tensors and %d attention projections, one MLP tensor and two projections per thread" \
+              % (nthreads, 2 * nthreads)
+    else:
+        idx = sorted(range(w.n), key=lambda t: -w.numel[t])[:2 * nthreads]
+        how = "the %d largest tensors" % len(idx)
+    idx.sort(key=lambda t: -w.numel[t])  # largest first onto the thread pool
     sub = w.subset(idx)
     weights = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in W.init_weights(sub, device)]
     grads = [W.grad_tensor(sub, t, 1, device).cpu().numpy() for t in range(sub.n)]
     states = [O.TensorState(x, w.level) for x in weights]
-    nthreads = max(1, min(threads, len(idx)))
-    # one thread on the first tensor of the sample (fresh state, same inputs)
-    one = O.TensorState(weights[0].copy(), w.level)
+    # one thread on the last (smallest) tensor of the sample (fresh state, same inputs)
+    one = O.TensorState(weights[-1].copy(), w.level)
     t0 = time.perf_counter()
-    O.step_list([one], grads[:1], w.grad_fmt, 1, threads=1, **w.hparams())
+    O.step_list([one], grads[-1:], w.grad_fmt, 1, threads=1, **w.hparams())
     dt1 = time.perf_counter() - t0
     t0 = time.perf_counter()
     O.step_list(states, grads, w.grad_fmt, 1, threads=nthreads, **w.hparams())
@@ -303,12 +317,11 @@ def cpu_baseline(w, device, threads: int) -> dict:
         pass
     return {"value": sub.params / dt, "unit": "params/s", "cores": nthreads, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": "%d tensors (%s), %d params, one step (grad amax + quantize + %s step), "
-                      "one oracle thread per tensor" % (sub.n, ", ".join(sub.names[:3]) + ", ...",
-                                                         sub.params, w.level),
-            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
-            "one_thread": {"value": sub.numel[0] / dt1, "unit": "params/s",
-                           "sample": "%s (%d params)" % (sub.names[0], sub.numel[0])},
+            "sample": "%d tensors of the list (%s), %d params, one step each (grad amax + quantize + %s "
+                      "step), on a pool of %d threads" % (sub.n, how, sub.params, w.level, nthreads),
+            "threads": nthreads, "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "one_thread": {"value": sub.numel[-1] / dt1, "unit": "params/s",
+                           "sample": "%s (%d params)" % (sub.names[-1], sub.numel[-1])},
             "full_step_seconds_extrapolated": round(w.params / (sub.params / dt), 2)}
 
 
@@ -336,6 +349,8 @@ def _kind_of(name: str):
         return "o3_pass3", PASS3_BYTES
     if fn == "k_quantize_pass1":
         return "quantize_pass1", QUANTIZE_PASS1_BYTES
+    if fn == "k_stream_probe":  # <copy>: measurement streams (bytes are not per parameter)
+        return ("copy_probe" if targs and targs[0] == "true" else "read_probe"), 0
     if fn == "k_rmw_probe":
         return "rmw_probe", PASS2_BYTES
     if fn == "k_scaled_v_pass1":  # also reads the FP16 second moment
@@ -438,6 +453,8 @@ def summarize_profiles(dirs, workload: str) -> None:
         if kb is None:
             continue
         kind, bpp = kb
+        if not bpp:
+            continue  # measurement streams (run only when profiling is on)
         f = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [0])))
         wr = sum(write.get(name, [0])) / max(1, len(write.get(name, [0])))
         hbm = f * 1024 * ffac + wr * 1024 * wfac
@@ -466,7 +483,7 @@ def summarize_profiles(dirs, workload: str) -> None:
                 continue
             kb = _kind_of(r["Name"])
             avg = float(r["AverageNs"]) * 1e-6
-            gbps = kb[1] * w.params / (avg * 1e-3) / 1e9 if kb else float("nan")
+            gbps = kb[1] * w.params / (avg * 1e-3) / 1e9 if kb and kb[1] else float("nan")
             m = re.search(r"\b(k_\w+)", r["Name"])
             short = kb[0] if kb else (m.group(1) if m else r["Name"][:40])
             tl.append("| %s | %s | %.4f | %.4f | %.4f | %.1f |" % (short, r["Calls"], avg,
@@ -547,13 +564,19 @@ def main() -> int:
     if not args.no_profile:
         M.profile_select([dom])
         M.profile_enable(True)
+    # one event per step boundary on the launch stream (for the median step
+    # time; an event between steps costs nothing measurable at these sizes)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step += 1
         st.step(step)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     kernels = {}
     if not args.no_profile:
         M.profile_enable(False)
@@ -666,6 +689,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2] if len(step_ms) % 2
+                                    else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2]), 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
