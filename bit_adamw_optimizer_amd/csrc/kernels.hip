@@ -119,9 +119,16 @@ __global__ __launch_bounds__(kBlock) void k_amax(const TensorDesc* __restrict__ 
         m = umax(m, umax(umax(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu),
                          umax(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu)));
     } else {
+      // partial tile: whole 4-element groups as one 16-byte access, the
+      // group holding the tensor's end element by element
       for (int k = 0; k < 4; ++k) {
         const int64_t e = group4_base(tile, k);
-        for (int64_t i = e; i < e + 4 && i < r.end; ++i) m = umax(m, abs_bits(x[i]));
+        if (e + 4 <= r.end) {
+          const u32x4 v = load_stream<u32x4>(x + e);
+          m = umax(m, umax(umax(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), umax(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+        } else {
+          for (int64_t i = e; i < r.end; ++i) m = umax(m, abs_bits(x[i]));
+        }
       }
     }
   }
@@ -165,7 +172,14 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const TensorDesc* __restric
     } else {
       for (int k = 0; k < 4; ++k) {
         const int64_t e = group4_base(tile, k);
-        for (int64_t i = e; i < e + 4 && i < r.end; ++i) q[i] = (uint8_t)enc1_nan<FMT>(x[i] * s);
+        if (e + 4 <= r.end) {
+          const u32x4 v = load_stream<u32x4>(x + e);
+          float f[4] = {__uint_as_float(v.x) * s, __uint_as_float(v.y) * s, __uint_as_float(v.z) * s,
+                        __uint_as_float(v.w) * s};
+          store_stream<uint32_t>(q + e, enc4_nan<FMT>(f));
+        } else {
+          for (int64_t i = e; i < r.end; ++i) q[i] = (uint8_t)enc1_nan<FMT>(x[i] * s);
+        }
       }
     }
   }
@@ -196,7 +210,18 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const TensorDesc* __restr
     } else {
       for (int k = 0; k < 4; ++k) {
         const int64_t e = group4_base(tile, k);
-        for (int64_t i = e; i < e + 4 && i < r.end; ++i) out[i] = dec1<FMT>(q[i]) * si;
+        if (e + 4 <= r.end) {
+          float f[4];
+          dec4<FMT>(load<uint32_t>(q + e), f);
+          u32x4 o;
+          o.x = __float_as_uint(f[0] * si);
+          o.y = __float_as_uint(f[1] * si);
+          o.z = __float_as_uint(f[2] * si);
+          o.w = __float_as_uint(f[3] * si);
+          store<u32x4>(out + e, o);
+        } else {
+          for (int64_t i = e; i < r.end; ++i) out[i] = dec1<FMT>(q[i]) * si;
+        }
       }
     }
   }
@@ -253,16 +278,26 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
         const float ge = effective_grad<COUPLED>(k, g[e] * gsi, w[e]);
         mx = umax(mx, abs_bits(first_moment(k, ge, m[e] * msi)));
       }
-    } else if (!COUPLED) {
-      const int64_t e = group16_base(tile);
-      for (int64_t i = e; i < e + 16 && i < r.end; ++i)
-        mx = umax(mx, abs_bits(first_moment(k, dec1<GF>(gq[i]) * gsi, dec1<kE4M3>(mq[i]) * msi)));
     } else {
+      // partial tile: whole 8-element groups as vector accesses, the group
+      // holding the tensor's end element by element
       for (int h = 0; h < 2; ++h) {
-        const int64_t e = h ? e1 : e0;
-        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
-          const float ge = effective_grad<COUPLED>(k, dec1<GF>(gq[i]) * gsi, COUPLED ? h_to_f(wh[i]) : 0.0f);
-          mx = umax(mx, abs_bits(first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi)));
+        const int64_t e = COUPLED ? (h ? e1 : e0) : group16_base(tile) + 8 * h;
+        if (e + 8 <= r.end) {
+          float g[8], m[8], w[8];
+          dec8<GF>(load<u32x2>(gq + e), g);
+          dec8<kE4M3>(load<u32x2>(mq + e), m);
+          if (COUPLED) h8_to_f8(load<u32x4>(wh + e), w);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float ge = effective_grad<COUPLED>(k, g[i] * gsi, COUPLED ? w[i] : 0.0f);
+            mx = umax(mx, abs_bits(first_moment(k, ge, m[i] * msi)));
+          }
+        } else {
+          for (int64_t i = e; i < r.end; ++i) {
+            const float ge = effective_grad<COUPLED>(k, dec1<GF>(gq[i]) * gsi, COUPLED ? h_to_f(wh[i]) : 0.0f);
+            mx = umax(mx, abs_bits(first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi)));
+          }
         }
       }
     }
@@ -319,10 +354,23 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __r
     } else {
       for (int j = 0; j < 4; ++j) {
         const int64_t e = group4_base(tile, j);
-        for (int64_t i = e; i < e + 4 && i < r.end; ++i) {
-          const uint32_t c = enc1_nan<GF>(x[i] * s);
-          q[i] = (uint8_t)c;
-          mx = umax(mx, abs_bits(first_moment(k, dec1<GF>((uint8_t)c) * gsi, dec1<kE4M3>(mq[i]) * msi)));
+        if (e + 4 <= r.end) {
+          const u32x4 v = load_stream<u32x4>(x + e);
+          const float f[4] = {__uint_as_float(v.x) * s, __uint_as_float(v.y) * s, __uint_as_float(v.z) * s,
+                              __uint_as_float(v.w) * s};
+          const uint32_t c = enc4_nan<GF>(f);
+          store_stream<uint32_t>(q + e, c);
+          float g[4], m[4];
+          dec4<GF>(c, g);
+          dec4<kE4M3>(load_stream<uint32_t>(mq + e), m);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = umax(mx, abs_bits(first_moment(k, g[i] * gsi, m[i] * msi)));
+        } else {
+          for (int64_t i = e; i < r.end; ++i) {
+            const uint32_t c = enc1_nan<GF>(x[i] * s);
+            q[i] = (uint8_t)c;
+            mx = umax(mx, abs_bits(first_moment(k, dec1<GF>((uint8_t)c) * gsi, dec1<kE4M3>(mq[i]) * msi)));
+          }
         }
       }
     }
@@ -449,9 +497,17 @@ __global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restric
     } else {
       for (int h = 0; h < 2; ++h) {
         const int64_t e = h ? e1 : e0;
-        for (int64_t i = e; i < e + 8 && i < r.end; ++i) {
-          float ww[4] = {h_to_f(wh[i]) * s_w, 0.0f, 0.0f, 0.0f};
-          w8[i] = (uint8_t)(enc4<kE4M3>(ww) & 0xFFu);
+        if (e + 8 <= r.end) {
+          float w[8];
+          h8_to_f8(load_stream<u32x4>(wh + e), w);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = w[i] * s_w;
+          store_stream<u32x2>(w8 + e, enc8<kE4M3>(w));
+        } else {
+          for (int64_t i = e; i < r.end; ++i) {
+            float ww[4] = {h_to_f(wh[i]) * s_w, 0.0f, 0.0f, 0.0f};
+            w8[i] = (uint8_t)(enc4<kE4M3>(ww) & 0xFFu);
+          }
         }
       }
     }
