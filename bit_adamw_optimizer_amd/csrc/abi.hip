@@ -190,6 +190,14 @@ void evict_locked(PlanCache& c) {
   }
 }
 
+// Elements per chunk of a list: whole tiles, fewer per chunk for a small
+// list so that its launches still spread over every compute unit.
+int64_t list_chunk_elems(int32_t n, const int64_t* numel) {
+  int64_t tiles = 0;
+  for (int32_t t = 0; t < n; ++t) tiles += (numel[t] + kTile - 1) / kTile;
+  return chunk_tiles_for(tiles) * kTile;
+}
+
 // Returns the plan of a tensor list, building and uploading it (on 'stream')
 // the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n, or
 // null for a role the operation does not have): roles 0..4 fill p0..p4 of
@@ -237,11 +245,12 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
       }
   }
 
-  // Build the chunk map.
+  // Build the chunk map (chunks of list_chunk_elems elements).
+  const int64_t ce = list_chunk_elems(n, numel);
   std::vector<ChunkRef> chunks;
   int64_t total = 0;
   for (int32_t t = 0; t < n; ++t) {
-    int64_t k = (numel[t] + kChunk - 1) / kChunk;
+    int64_t k = (numel[t] + ce - 1) / ce;
     if (k == 0 && min_one_chunk) k = 1;
     if (k > INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "tensor too large for the chunk map");
     total += k;
@@ -249,7 +258,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   if (total > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks for one launch");
   chunks.reserve((size_t)total);
   for (int32_t t = 0; t < n; ++t) {
-    int64_t k = (numel[t] + kChunk - 1) / kChunk;
+    int64_t k = (numel[t] + ce - 1) / ce;
     if (k == 0 && min_one_chunk) k = 1;
     for (int64_t j = 0; j < k; ++j) chunks.push_back({t, (int32_t)j});
   }
@@ -281,6 +290,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
     TensorDesc d;
     std::memset(&d, 0, sizeof d);
     d.numel = numel[t];
+    d.chunk = ce;
     const void* p[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
     for (int r = 0; r < nroles && r < 6; ++r) p[r] = ptrs[r] ? ptrs[r][t] : nullptr;
     d.p0 = p[0];
@@ -661,12 +671,13 @@ constexpr int kNoAllocMaxDevices = 64;
 // chunk map, each section 256-byte aligned.
 struct NoAllocLayout {
   size_t scratch_bytes = 0, desc_bytes = 0, chunk_bytes = 0, total = 0;
-  int64_t nchunks = 0;
+  int64_t nchunks = 0, chunk_elems = kChunk;
 };
 
 msamp_status noalloc_layout(int32_t n, const int64_t* numel, NoAllocLayout* l) {
+  l->chunk_elems = list_chunk_elems(n, numel);
   int64_t chunks = 0;
-  for (int32_t t = 0; t < n; ++t) chunks += (numel[t] + kChunk - 1) / kChunk;
+  for (int32_t t = 0; t < n; ++t) chunks += (numel[t] + l->chunk_elems - 1) / l->chunk_elems;
   l->nchunks = chunks;
   l->scratch_bytes = align_up(sizeof(uint32_t) * 2 * (size_t)n, 256);
   l->desc_bytes = align_up(sizeof(TensorDesc) * (size_t)n, 256);
@@ -675,8 +686,8 @@ msamp_status noalloc_layout(int32_t n, const int64_t* numel, NoAllocLayout* l) {
   if (l->total > kNoAllocScratchBytes)
     return fail(MSAMP_E_INVALID_ARG,
                 "the tensor list needs " + std::to_string(l->total) + " bytes of tables (" +
-                    std::to_string(n) + " tensors, " + std::to_string(chunks) +
-                    " chunks of 65536 elements); msamp_adamw_o2_step_noalloc holds at most " +
+                    std::to_string(n) + " tensors, " + std::to_string(chunks) + " chunks of " +
+                    std::to_string(l->chunk_elems) + " elements); msamp_adamw_o2_step_noalloc holds at most " +
                     std::to_string(kNoAllocScratchBytes));
   return MSAMP_OK;
 }
@@ -773,6 +784,7 @@ msamp_status step_noalloc_impl(int32_t n, const int64_t* numel, const uint8_t* c
     TensorDesc d;
     std::memset(&d, 0, sizeof d);
     d.numel = numel[t];
+    d.chunk = l.chunk_elems;
     d.p0 = grad[t];
     d.p1 = exp_avg[t];
     d.p2 = exp_avg_sq[t];
@@ -781,7 +793,7 @@ msamp_status step_noalloc_impl(int32_t n, const int64_t* numel, const uint8_t* c
   }
   ChunkRef* hc = (ChunkRef*)(hb + l.scratch_bytes + l.desc_bytes);
   for (int32_t t = 0, i = 0; t < n; ++t)
-    for (int64_t j = 0, k = (numel[t] + kChunk - 1) / kChunk; j < k; ++j) hc[i++] = {t, (int32_t)j};
+    for (int64_t j = 0, k = (numel[t] + l.chunk_elems - 1) / l.chunk_elems; j < k; ++j) hc[i++] = {t, (int32_t)j};
   // From pageable host memory the copy is synchronous: when it returns, the
   // earlier work on the stream has finished and the image has been read.
   e = hipMemcpyAsync(base, hb, l.total, hipMemcpyHostToDevice, s);

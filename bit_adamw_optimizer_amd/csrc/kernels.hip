@@ -78,9 +78,10 @@ __device__ __forceinline__ ChunkRange chunk_range(const ChunkRef* chunks, const 
   const ChunkRef c = chunks[blockIdx.x];
   ChunkRange r;
   r.t = c.tensor;
-  r.begin = (int64_t)c.chunk * kChunk;
+  const int64_t ce = desc[c.tensor].chunk;
+  r.begin = (int64_t)c.chunk * ce;
   const int64_t n = desc[c.tensor].numel;
-  r.end = r.begin + kChunk < n ? r.begin + kChunk : n;
+  r.end = r.begin + ce < n ? r.begin + ce : n;
   return r;
 }
 

@@ -10,11 +10,23 @@
 namespace msamp {
 
 // Launch geometry. One workgroup of kBlock threads (4 waves) owns one chunk
-// of at most kChunk consecutive elements of one tensor and walks it in tiles
-// of kTile elements, 16 per thread and 1024 per wave.
+// of consecutive elements of one tensor and walks it in tiles of kTile
+// elements, 16 per thread and 1024 per wave. A chunk is kChunk elements
+// (16 tiles), or fewer tiles for a list too small to give every compute
+// unit several chunks of that size (chunk_tiles_for); the descriptor of
+// each tensor carries the chunk size of its list.
 constexpr int kBlock = 256;
 constexpr int64_t kTile = (int64_t)kBlock * 16;
-constexpr int64_t kChunk = 16 * kTile;  // 65536 elements
+constexpr int64_t kMaxChunkTiles = 16;
+constexpr int64_t kChunk = kMaxChunkTiles * kTile;  // 65536 elements
+
+// Tiles per chunk for a list of 'total_tiles' tiles: 16, unless that gives
+// fewer than 4 chunks per compute unit of a 256-CU device; then
+// total_tiles / 1024, at least 1.
+inline int64_t chunk_tiles_for(int64_t total_tiles) {
+  const int64_t t = total_tiles / (256 * 4);
+  return t < 1 ? 1 : (t > kMaxChunkTiles ? kMaxChunkTiles : t);
+}
 
 // Multi-tensor-apply descriptor of one tensor (64 bytes). The roles of the
 // pointers depend on the operation:
@@ -34,7 +46,7 @@ struct TensorDesc {
   void* p4;
   int64_t numel;
   const void* aux;
-  int64_t reserved;
+  int64_t chunk;  // elements per chunk of this tensor's list (a multiple of kTile)
 };
 static_assert(sizeof(TensorDesc) == 64, "descriptor must stay 64 bytes");
 

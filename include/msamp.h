@@ -216,13 +216,16 @@ msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t*
  * allocate device memory (tight serving loops, harnesses that forbid
  * hipMalloc): the same kernels, bit-identical results, and no allocation of
  * any kind in the call. Its tables (two u32 amax words per tensor, the
- * 64-byte descriptor of each tensor, 8 bytes per 65,536-element chunk) live
+ * 64-byte descriptor of each tensor, 8 bytes per chunk of C elements) live
  * in a static device array of 4 MiB (MSAMP_NOALLOC_SCRATCH_BYTES) that each
  * device holds from its first call until the process ends. They are rebuilt
  * and copied into it on every call, synchronously: the call returns once
  * the earlier work on the stream has finished and the copy is done, then
  * the kernels run asynchronously as usual.
- * Limit: round256(8 n) + round256(64 n) + 8 * sum_t ceil(numel[t] / 65536)
+ * C = 4096 * clamp(floor(T / 1024), 1, 16) with T = sum_t ceil(numel[t] /
+ * 4096): 65,536, or fewer for a list under 16,384 tiles (about 67M
+ * elements), so that small lists still spread over every compute unit.
+ * Limit: round256(8 n) + round256(64 n) + 8 * sum_t ceil(numel[t] / C)
  * <= MSAMP_NOALLOC_SCRATCH_BYTES (the Llama-2-13B list, 363 tensors and
  * 13.0e9 parameters, needs 1.6 MB); a larger list returns
  * MSAMP_E_INVALID_ARG before any device work.

@@ -155,6 +155,20 @@ def test_ragged_sizes_o2_and_o3():
                 assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
 
 
+def test_mid_size_list_takes_3_tile_chunks():
+    """A list of 3,126 tiles of 4,096 elements is split into chunks of 3
+    tiles (12,288 elements: small lists get smaller chunks so that every
+    compute unit has work); O2 and O3 against the oracle."""
+    sizes = [6_000_001, 4_500_007, 2_300_000]
+    tiles = sum(-(-k // 4096) for k in sizes)
+    assert tiles // 1024 == 3
+    for level in ("O2", "O3"):
+        w = W.Workload("mid_" + level, level, W.E4M3, 3, ["a", "b", "c"], sizes, seed_base=17)
+        stats, _, _ = run_parity(w, 3)
+        _report(w.name, stats)
+        assert_bar(stats)
+
+
 def test_gpt2_small_o2_10_steps():
     w = W.make("gpt2_small")
     log("gpt2_small O2, %d tensors, %d params" % (w.n, w.params))
