@@ -119,6 +119,7 @@ struct Plan {
   size_t bytes = 0;
   uint32_t* scratch_a = nullptr;
   uint32_t* scratch_b = nullptr;
+  uint32_t* done = nullptr;  // finished chunks per tensor (folded meta writes), zero between calls
   TensorDesc* desc = nullptr;
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
@@ -266,7 +267,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   auto plan = std::make_unique<Plan>();
   plan->device = dev;
   plan->key = std::move(key);
-  const size_t scratch_bytes = align_up(sizeof(uint32_t) * 2 * (size_t)std::max(n, 1), 256);
+  const size_t scratch_bytes = align_up(sizeof(uint32_t) * 3 * (size_t)std::max(n, 1), 256);
   const size_t desc_bytes = align_up(sizeof(TensorDesc) * (size_t)std::max(n, 1), 256);
   const size_t chunk_bytes = align_up(sizeof(ChunkRef) * std::max<size_t>(chunks.size(), 1), 256);
   plan->bytes = scratch_bytes + desc_bytes + chunk_bytes;
@@ -307,6 +308,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   char* db = (char*)plan->dev;
   plan->scratch_a = (uint32_t*)db;
   plan->scratch_b = (uint32_t*)db + std::max(n, 1);
+  plan->done = (uint32_t*)db + 2 * (size_t)std::max(n, 1);
   plan->desc = (TensorDesc*)(db + scratch_bytes);
   plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
   plan->nchunks = (int64_t)chunks.size();
@@ -412,6 +414,27 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
     if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
   } while (0)
 
+// Lists of at most this many chunks write their meta records from the
+// workgroup that completes each tensor (one launch fewer per pass that ends
+// in meta: the launch costs more than the work there); larger lists keep a
+// finalize launch, which avoids one counter atomic per workgroup.
+constexpr int64_t kFoldMaxChunks = 8192;
+
+// The meta writes of a step folded into its last pass (pass 2 for O2,
+// pass 3 for O3), or none for a large list.
+MetaFold step_fold(const Plan* p, bool o3, msamp_meta* exp_avg_meta, msamp_meta* weight_fp8_meta) {
+  MetaFold f;
+  if (p->nchunks > kFoldMaxChunks) return f;
+  f.done = p->done;
+  f.meta_a = exp_avg_meta;
+  f.amax_a = p->scratch_a;
+  if (o3) {
+    f.meta_b = weight_fp8_meta;
+    f.amax_b = p->scratch_b;
+  }
+  return f;
+}
+
 // The tensor lists and meta arrays of an O2 (o3 = false) or O3 step.
 msamp_status check_step_lists(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
                               const msamp_meta* grad_meta, uint8_t* const* exp_avg,
@@ -440,7 +463,7 @@ msamp_status step_plan(bool o3, int32_t n, const int64_t* numel, const uint8_t* 
   const void* const* roles[5] = {(const void* const*)grad, (const void* const*)exp_avg,
                                  (const void* const*)exp_avg_sq, (const void* const*)weight,
                                  (const void* const*)weight_fp8};
-  return get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, false, s, p, lease);
+  return get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, true, s, p, lease);
 }
 
 msamp_status check_amax_array(int32_t n, const float* a, const char* role) {
@@ -475,15 +498,17 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, k, s, kdev));
+  const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev));
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev, o3 ? MetaFold{} : fold));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
-  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
-               launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
-                                    o3 ? weight_fp8_meta : nullptr, 448.0f, s));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold));
+  if (fold.done == nullptr)
+    MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+                 launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
+                                      o3 ? weight_fp8_meta : nullptr, 448.0f, s));
   return MSAMP_OK;
 }
 
@@ -510,20 +535,23 @@ msamp_status quantize_step_impl(bool o3, int32_t n, const int64_t* numel, const 
   if (!o3) roles[4] = nullptr;
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, 6, false, s, &p, &lease));
+  MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, 6, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE_PASS1, s,
                launch_quantize_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
                                      p->scratch_a, k, s));
+  const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, false, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s));
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, nullptr,
+                                 o3 ? MetaFold{} : fold));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s));
-  MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
-               launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
-                                    o3 ? weight_fp8_meta : nullptr, 448.0f, s));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold));
+  if (fold.done == nullptr)
+    MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
+                 launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
+                                      o3 ? weight_fp8_meta : nullptr, 448.0f, s));
   return MSAMP_OK;
 }
 
@@ -550,7 +578,7 @@ msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* 
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_scaled_v_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -586,7 +614,7 @@ msamp_status step_delayed_impl(int32_t n, const int64_t* numel, const uint8_t* c
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_O2_DELAYED, s,
                launch_step_delayed(grad_fmt, false, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -856,9 +884,16 @@ msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel, 
     const void* const* roles[1] = {(const void* const*)x};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, false, s, &p, &lease));
-    MSAMP_LAUNCH(MSAMP_KERNEL_AMAX, s, launch_amax(p->desc, p->chunks, p->nchunks, p->scratch_a, s));
-    MSAMP_LAUNCH(MSAMP_KERNEL_AMAX_FINALIZE, s, launch_amax_finalize(n, p->scratch_a, meta, s));
+    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, true, s, &p, &lease));
+    MetaFold fold;  // small lists: the completing workgroup writes meta[t].amax
+    if (p->nchunks <= kFoldMaxChunks) {
+      fold.done = p->done;
+      fold.meta_a = meta;
+      fold.amax_a = p->scratch_a;
+    }
+    MSAMP_LAUNCH(MSAMP_KERNEL_AMAX, s, launch_amax(p->desc, p->chunks, p->nchunks, p->scratch_a, s, fold));
+    if (fold.done == nullptr)
+      MSAMP_LAUNCH(MSAMP_KERNEL_AMAX_FINALIZE, s, launch_amax_finalize(n, p->scratch_a, meta, s));
     return MSAMP_OK;
   });
 }
@@ -1236,7 +1271,7 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
                                    (const void* const*)exp_avg_sq, (const void* const*)weight};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launch is enqueued
-    MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, false, s, &p, &lease));
+    MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s));
     return MSAMP_OK;
   });

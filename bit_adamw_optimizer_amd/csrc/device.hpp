@@ -76,6 +76,15 @@ __device__ __forceinline__ void atomic_max_if_larger(uint32_t m, uint32_t* dst) 
     atomicMax(dst, m);
 }
 
+// The same, returning only once the word is known to be at least m: the
+// atomic's returned value is waited for (or the coherent load already saw a
+// value at least m), so a later atomic of this thread is performed after it.
+__device__ __forceinline__ void atomic_max_if_larger_wait(uint32_t m, uint32_t* dst) {
+  uint32_t seen = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (m != 0u && m > seen) seen = atomicMax(dst, m);
+  asm volatile("" ::"v"(seen));
+}
+
 // Largest value over a workgroup of BS threads, returned to every thread.
 // The closing barrier keeps a later reduction from overwriting the LDS
 // partials before every thread has read them.

@@ -34,6 +34,9 @@ namespace {
 // Largest value of the workgroup, folded into *dst. The closing barrier
 // keeps a later reduction of the same workgroup from overwriting the LDS
 // partials before thread 0 has read them.
+// WAIT: thread 0 waits until its update has been performed (the folded
+// meta write of the same launch counts this workgroup only after that).
+template <bool WAIT = false>
 __device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
   __shared__ uint32_t partial[kBlock / 64];
   v = wave_max(v);
@@ -43,7 +46,10 @@ __device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
     uint32_t m = partial[0];
 #pragma unroll
     for (int k = 1; k < kBlock / 64; ++k) m = umax(m, partial[k]);
-    atomic_max_if_larger(m, dst);
+    if (WAIT)
+      atomic_max_if_larger_wait(m, dst);
+    else
+      atomic_max_if_larger(m, dst);
   }
   __syncthreads();
 }
@@ -85,6 +91,55 @@ __device__ __forceinline__ ChunkRange chunk_range(const ChunkRef* chunks, const 
   return r;
 }
 
+// Chunks of a tensor in a plan that folds the meta writes (at least one).
+__device__ __forceinline__ uint32_t chunks_of(const TensorDesc& d) {
+  return d.numel == 0 ? 1u : (uint32_t)((d.numel + d.chunk - 1) / d.chunk);
+}
+
+__device__ __forceinline__ void put_meta(msamp_meta* meta, float amax, float fmax) {
+  const float s = scale_rule(amax, fmax);
+  msamp_meta m;
+  m.amax = amax;
+  m.scale = s;
+  m.scale_inv = 1.0f / s;
+  m.reserved = 0.0f;
+  *meta = m;
+}
+
+__device__ __forceinline__ uint32_t take_word(uint32_t* p) {
+  const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// Called by all threads of every workgroup after its last use of tensor t's
+// data and amax words; the workgroup whose count completes the tensor
+// writes the meta records: the full record {amax, scale, 1/scale} (E4M3
+// range, for meta_a and meta_b), or only the amax field of meta_a when
+// AMAX_ONLY. The amax and count words are only touched with device-scope
+// atomics, which are performed at one coherence point; no fence is used (on
+// gfx950 a device-scope fence writes back the whole L2 of the XCD).
+// When the same launch raised the amax word (AMAX_ONLY: the amax kernel),
+// thread 0 issued that atomic and waited for it (block_max_into<true>), so
+// its update has been performed before its chunk is counted. Every other
+// read of the words happened before the workgroup's count (the reads fed
+// the work done since).
+template <bool AMAX_ONLY>
+__device__ __forceinline__ void fold_meta(const MetaFold& f, const TensorDesc* desc, int t) {
+  if (f.done == nullptr) return;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const uint32_t before = __hip_atomic_fetch_add(&f.done[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (before + 1u != chunks_of(desc[t])) return;
+  const float a = __uint_as_float(take_word(&f.amax_a[t]));
+  if (AMAX_ONLY)
+    f.meta_a[t].amax = a;
+  else
+    put_meta(&f.meta_a[t], a, kE4M3Max);
+  if (f.meta_b != nullptr) put_meta(&f.meta_b[t], __uint_as_float(take_word(&f.amax_b[t])), kE4M3Max);
+  __hip_atomic_store(&f.done[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // First element of this lane's 8-element groups (FP8/FP16 layout) in the
 // tile starting at 'tile': e0 and e0 + 512.
 __device__ __forceinline__ int64_t group8_base(int64_t tile) {
@@ -106,7 +161,7 @@ __device__ __forceinline__ int64_t group4_base(int64_t tile, int k) {
 
 __global__ __launch_bounds__(kBlock) void k_amax(const TensorDesc* __restrict__ desc,
                                                  const ChunkRef* __restrict__ chunks,
-                                                 uint32_t* __restrict__ scratch) {
+                                                 uint32_t* __restrict__ scratch, MetaFold fold) {
   const ChunkRange r = chunk_range(chunks, desc);
   const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].p0);
   uint32_t m = 0u;
@@ -133,7 +188,11 @@ __global__ __launch_bounds__(kBlock) void k_amax(const TensorDesc* __restrict__ 
       }
     }
   }
-  block_max_into(m, &scratch[r.t]);
+  if (fold.done != nullptr)
+    block_max_into<true>(m, &scratch[r.t]);
+  else
+    block_max_into(m, &scratch[r.t]);
+  fold_meta<true>(fold, desc, r.t);
 }
 
 __global__ __launch_bounds__(kBlock) void k_amax_finalize(int32_t n, uint32_t* __restrict__ scratch,
@@ -394,7 +453,8 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
                                                        const uint32_t* __restrict__ amax_m,
                                                        uint32_t* __restrict__ amax_w,
                                                        StepConsts kv,
-                                                       const StepConsts* __restrict__ kdev) {
+                                                       const StepConsts* __restrict__ kdev,
+                                                       MetaFold fold) {
   static_assert(!(O3 && DELAYED), "the delayed-scaling ablation is O2 only");
   const StepConsts k = kdev != nullptr ? *kdev : kv;
   const ChunkRange r = chunk_range(chunks, desc);
@@ -475,12 +535,13 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
     block_max_into(bits, &amax_w[r.t]);
   }
   if (DELAYED) block_max_into(mmax, &amax_w[r.t]);
+  if (!O3 && !DELAYED) fold_meta<false>(fold, desc, r.t);  // O3: the fold is in pass 3
 }
 
 // Pass 3 (O3): FP8 E4M3 copy of the stored master with its own scale.
 __global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restrict__ desc,
                                                      const ChunkRef* __restrict__ chunks,
-                                                     const uint32_t* __restrict__ amax_w) {
+                                                     const uint32_t* __restrict__ amax_w, MetaFold fold) {
   const ChunkRange r = chunk_range(chunks, desc);
   const float s_w = scale_rule(__uint_as_float(amax_w[r.t]), kE4M3Max);
   const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
@@ -513,6 +574,7 @@ __global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restric
       }
     }
   }
+  fold_meta<false>(fold, desc, r.t);
 }
 
 __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* __restrict__ amax_a,
@@ -827,9 +889,9 @@ inline unsigned grid_of(int64_t nchunks) { return (unsigned)nchunks; }
 // ------------------------------------------------------------ launchers ---
 
 hipError_t launch_amax(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                       uint32_t* scratch, hipStream_t stream) {
+                       uint32_t* scratch, hipStream_t stream, const MetaFold& fold) {
   if (nchunks <= 0) return hipSuccess;
-  k_amax<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, scratch);
+  k_amax<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, scratch, fold);
   return hipGetLastError();
 }
 
@@ -898,35 +960,36 @@ hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, con
 template <int GF, bool O3, bool COUPLED>
 static void pass2_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, const uint32_t* amax_m,
-                         uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev) {
+                         uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev, const MetaFold& fold) {
   k_step_pass2<GF, O3, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k,
-                                                          kdev);
+                                                          kdev, fold);
 }
 
 template <int GF>
 static void pass2_dispatch(bool o3, bool coupled, unsigned g, hipStream_t stream,
                            const TensorDesc* desc, const ChunkRef* chunks, const msamp_meta* gmeta,
                            const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                           const StepConsts& k, const StepConsts* kdev) {
+                           const StepConsts& k, const StepConsts* kdev, const MetaFold& f) {
   if (o3) {
-    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
-    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
   } else {
-    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
-    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
   }
 }
 
 hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* desc,
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                             const StepConsts& k, hipStream_t stream, const StepConsts* kdev) {
+                             const StepConsts& k, hipStream_t stream, const StepConsts* kdev,
+                             const MetaFold& fold) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3)
-    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
   else
-    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev);
+    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
   return hipGetLastError();
 }
 
@@ -937,14 +1000,14 @@ hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, c
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3) {
     if (coupled)
-      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
+      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
     else
-      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
+      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
   } else {
     if (coupled)
-      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
+      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
     else
-      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr);
+      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
   }
   return hipGetLastError();
 }
@@ -983,9 +1046,9 @@ hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* me
 }
 
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                           const uint32_t* amax_w, hipStream_t stream) {
+                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold) {
   if (nchunks <= 0) return hipSuccess;
-  k_o3_pass3<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, amax_w);
+  k_o3_pass3<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, amax_w, fold);
   return hipGetLastError();
 }
 

@@ -65,10 +65,27 @@ struct StepConsts {
   float b1, ob1, b2, ob2, eps, ss, ibs, dec, wd;
 };
 
+// Meta records written by the workgroup that completes each tensor instead
+// of by a separate finalize launch (used for small lists, where a launch
+// costs more than the work). 'done' counts the finished chunks of each
+// tensor (zero between calls; a plan that folds gives every tensor, also an
+// empty one, at least one chunk). The completing workgroup writes meta_a
+// from amax_a (and meta_b from amax_b when meta_b is set) and returns the
+// amax and count words to zero.
+struct MetaFold {
+  uint32_t* done = nullptr;  // null: no folding, a finalize launch follows
+  msamp_meta* meta_a = nullptr;
+  uint32_t* amax_a = nullptr;
+  msamp_meta* meta_b = nullptr;
+  uint32_t* amax_b = nullptr;
+};
+
 // Every launcher enqueues one kernel on 'stream' and returns the launch
 // status. 'nchunks' workgroups are launched (nothing when 0).
+// With fold.done set, the completing workgroup of each tensor writes
+// fold.meta_a[t].amax (only the amax field) from the scratch word.
 hipError_t launch_amax(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                       uint32_t* scratch, hipStream_t stream);
+                       uint32_t* scratch, hipStream_t stream, const MetaFold& fold = MetaFold{});
 hipError_t launch_amax_finalize(int32_t n, uint32_t* scratch, msamp_meta* meta,
                                 hipStream_t stream);
 // scale = scale_rule(meta.amax * world) (world = 1: the plain per-tensor
@@ -103,7 +120,7 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                              const StepConsts& k, hipStream_t stream,
-                             const StepConsts* kdev = nullptr);
+                             const StepConsts* kdev = nullptr, const MetaFold& fold = MetaFold{});
 // Ablation: the O2 update in one pass with delayed scaling of the first
 // moment (encode with scale(mmeta.amax) of the previous step; reduce the new
 // amax into amax_new).
@@ -115,7 +132,7 @@ hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, c
 hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* meta,
                                    hipStream_t stream);
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                           const uint32_t* amax_w, hipStream_t stream);
+                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold = MetaFold{});
 // meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then
 // amax_a[t] <- 0; the same for (amax_b, meta_b) when meta_b is not NULL,
 // with the range fmax_b (448 for an E4M3 copy, 65504 for a scaled FP16 v).

@@ -45,7 +45,10 @@ def test_bench_json_contract():
     assert all(c["GB/s"] > 0 for c in rf["ceilings"].values())
     # default: the gradient quantize runs fused with pass 1 (21 bytes per parameter)
     assert d["config"]["fused_quantize"] is True and d["bytes_per_param"] == 21
-    assert set(d["kernels"]) >= {"amax", "quantize_pass1", "o2_pass2", "finalize"}
+    assert set(d["kernels"]) >= {"amax", "quantize_pass1", "o2_pass2"}
+    # a list of under 8,192 chunks writes its meta records from the workgroup
+    # that completes each tensor: no finalize launches
+    assert "finalize" not in d["kernels"] and "amax_finalize" not in d["kernels"]
     assert d["optimizer_step"]["includes_grad_quantize"] is True
 
 
