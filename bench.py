@@ -90,6 +90,9 @@ def parse():
                    help="do not bracket kernels with HIP events")
     p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                    help="only run a device-to-device copy of this many GiB (counter calibration)")
+    p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
+                   help="write the profiles/ summary of a rocprofv3 run of SQ instruction counters "
+                        "(no GPU needed)")
     p.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR",
                                                             "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="write profiles/ summaries from rocprofv3 CSV output directories "
@@ -250,24 +253,25 @@ def numerics_report(st) -> dict:
     at +-max (0x7E). Counted over each role's one allocation in a few
     launches; the alignment padding between tensors holds zeros that no
     kernel writes, and is subtracted."""
-    n = sum(int(x.numel()) for x in st.tl_v.tensors)
-    v = storage_of(st.tl_v.tensors)
-    m = storage_of(st.tl_m.tensors)
-    pad_v, pad_m = v.numel() - n, m.numel() - n
-    vmag = v.view(torch_int16()) & 0x7FFF
-    zero = int((vmag == 0).sum()) - pad_v
-    sub = int(((vmag > 0) & (vmag < 0x0400)).sum())
-    mmag = m & 0x7F
-    m_zero = int((mmag == 0).sum()) - pad_m
-    m_max = int((mmag == 0x7E).sum())
-    return {"v_zero_frac": zero / n, "v_subnormal_frac": sub / n,
-            "m_code_zero_frac": m_zero / n, "m_code_max_frac": m_max / n}
-
-
-def torch_int16():
     import torch
 
-    return torch.int16
+    n = sum(int(x.numel()) for x in st.tl_v.tensors)
+    v = storage_of(st.tl_v.tensors).view(torch.int16)
+    m = storage_of(st.tl_m.tensors)
+    zero = sub = m_zero = m_max = 0
+    piece = 1 << 28  # bounded temporaries
+    for a in range(0, v.numel(), piece):
+        vmag = v[a:a + piece] & 0x7FFF
+        zero += int(torch.count_nonzero(vmag == 0))
+        sub += int(torch.count_nonzero((vmag > 0) & (vmag < 0x0400)))
+    for a in range(0, m.numel(), piece):
+        mmag = m[a:a + piece] & 0x7F
+        m_zero += int(torch.count_nonzero(mmag == 0))
+        m_max += int(torch.count_nonzero(mmag == 0x7E))
+    zero -= v.numel() - n
+    m_zero -= m.numel() - n
+    return {"v_zero_frac": zero / n, "v_subnormal_frac": sub / n,
+            "m_code_zero_frac": m_zero / n, "m_code_max_frac": m_max / n}
 
 
 def cpu_baseline(w, device, threads: int) -> dict:
@@ -493,6 +497,79 @@ def summarize_profiles(dirs, workload: str) -> None:
     print("wrote profiles for %s" % workload)
 
 
+SQ_COUNTERS = "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_WAVES"
+
+
+def summarize_sq(dirs, workload: str) -> None:
+    """profiles/ summary of a rocprofv3 run of SQ instruction counters: per
+    kernel, wave-level VALU and vector-memory instructions per element (x 64
+    lanes / parameters), and the VALU issue time at one wave64 VALU
+    instruction per compute unit per cycle (256 CUs at 2.4 GHz) beside the
+    kernel's time from the kernel-trace summary of the same sources."""
+    import csv
+    import glob
+
+    trace_dir, sq_dir = dirs
+    from bit_adamw_optimizer_amd import workloads as W
+    w = W.make(workload)
+
+    def rel(d):
+        return os.path.relpath(os.path.abspath(d), ROOT)
+
+    files = glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True)
+    agg = {}
+    for r in csv.DictReader(open(files[0])):
+        kb = _kind_of(r["Kernel_Name"])
+        if kb is None or not kb[1]:
+            continue
+        agg.setdefault(kb[0], {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+        agg[kb[0]][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    stats = glob.glob(os.path.join(trace_dir, "**", "*_kernel_stats.csv"), recursive=True)
+    kms = {}
+    for r in csv.DictReader(open(stats[0])):
+        kb = _kind_of(r["Name"])
+        if kb:
+            kms[kb[0]] = float(r["AverageNs"]) * 1e-6
+    args = None
+    for f in glob.glob(os.path.join(sq_dir, "*.log")):
+        for line in open(f, errors="replace"):
+            m = re.search(r"\[rocprofv3\] 'python3 \S*bench\.py([^']*)'", line)
+            if m:
+                args = m.group(1)
+    h = None
+    for f in glob.glob(os.path.join(sq_dir, "*.log")):
+        for line in open(f, errors="replace"):
+            if line.startswith("{") and "kernel_source_hash" in line:
+                h = json.loads(line)["kernel_source_hash"]
+    lines = ["# VALU and memory-instruction counters per launch, %s (%d params)" % (workload, w.params), "",
+             "Command (run from the repository root; R=$PWD; cd /tmp first):",
+             "  rocprofv3 --pmc %s -f csv -d $R/%s -o sq -- python3 $R/bench.py%s > $R/%s/bench.log 2>&1"
+             % (SQ_COUNTERS, rel(sq_dir), args or "", rel(sq_dir)),
+             "  python bench.py --summarize-sq %s %s --workload %s" % (rel(trace_dir), rel(sq_dir), workload), "",
+             "Kernel sources hash: %s" % h, "",
+             "Per element: wave-level instruction counts x 64 lanes / parameters. VALU issue time: one wave64",
+             "VALU instruction per CU per cycle (4 SIMDs, 4 cycles each), 256 CUs at 2.4 GHz; kernel time from",
+             "the kernel-trace summary (%s)." % rel(trace_dir), "",
+             "| kernel | launches | VALU instr / element | VMEM read instr / element | VMEM write instr / element "
+             "| VALU issue ms | kernel ms | VALU issue / kernel time |",
+             "|---|---|---|---|---|---|---|---|"]
+    for kind in sorted(agg):
+        c = agg[kind]
+
+        def mean(name):
+            v = list(c.get(name, {}).values())
+            return sum(v) / len(v) if v else float("nan")
+        valu, rd, wr = mean("SQ_INSTS_VALU"), mean("SQ_INSTS_VMEM_RD"), mean("SQ_INSTS_VMEM_WR")
+        issue_ms = valu / (256 * 2.4e9) * 1e3
+        kt = kms.get(kind, float("nan"))
+        lines.append("| %s | %d | %.2f | %.4f | %.4f | %.2f | %.2f | %.2f |"
+                     % (kind, len(c.get("SQ_INSTS_VALU", {})), valu * 64 / w.params, rd * 64 / w.params,
+                        wr * 64 / w.params, issue_ms, kt, issue_ms / kt))
+    with open(os.path.join(ROOT, "profiles", "path_kernels_%s_sq_counters.md" % workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("wrote the SQ summary for %s" % workload)
+
+
 def traffic_from_profiles(kernel: str, workload: str, params: int):
     """HBM bytes per launch from committed counter runs, when they were taken
     on the current kernel sources (else None)."""
@@ -512,6 +589,9 @@ def main() -> int:
     args = parse()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.workload)
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

@@ -425,7 +425,8 @@ def test_sharded_phases_equal_the_unsharded_step(level, adam, wl):
     every tensor, run the split-phase step; the per-tensor amaxes are
     combined with a MAX between the phases (what an all-reduce MAX over the
     ranks would do). Over 4 steps every byte of the state and every meta
-    record equals the unsharded step's."""
+    record equals the unsharded step's, and the sharded state meets the
+    parity bar against the oracle run on the whole tensors."""
     ranks = 3
     w = W.make(wl)
     if adam:
@@ -435,6 +436,9 @@ def test_sharded_phases_equal_the_unsharded_step(level, adam, wl):
     ref = GpuState(w, "cuda", adam=adam)
     sh = GpuState(w, "cuda", adam=adam)
     bounds = _slice_bounds(w.numel, ranks)
+    torch.cuda.synchronize()
+    ost = [O.TensorState(host(x), level, adam=adam) for x in sh.weights]
+    from tests.parity import Stats
 
     def piece(lst, r, kind):
         return M.TensorList([x[bounds[t][r]:bounds[t][r + 1]] for t, x in enumerate(lst)], kind)
@@ -483,3 +487,14 @@ def test_sharded_phases_equal_the_unsharded_step(level, adam, wl):
             assert torch.equal(d["mmeta"], ref.exp_avg_meta), s
             if level == "O3":
                 assert torch.equal(d["w8meta"], ref.weight_fp8_meta), s
+        # the sharded state against the oracle on the whole tensors
+        stats = {k: Stats() for k in ("m", "v", "w", "w8")}
+        for t in range(w.n):
+            qg, _ = O.step_tensor(ost[t], host(sh.grad_f32[t]), w.grad_fmt, s, **hp)
+            assert np.array_equal(host(sh.grad_q[t]), qg), (s, t)
+            stats["m"].add(host(sh.exp_avg[t]), ost[t].m, "fp8", "t%d" % t)
+            stats["v"].add(host(sh.exp_avg_sq[t]), ost[t].v, "f16", "t%d" % t)
+            stats["w"].add(host(sh.weights[t]), ost[t].w, "f16", "t%d" % t)
+            if level == "O3":
+                stats["w8"].add(host(sh.weight_fp8[t]), ost[t].w8, "fp8", "t%d" % t)
+        assert_bar(stats)
