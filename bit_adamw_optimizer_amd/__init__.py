@@ -655,19 +655,23 @@ def profile_read(kernel: str):
 
 # ----------------------------------------------------------- state helpers ---
 
-# Views into one allocation start at multiples of this many elements, which
-# keeps every view 16-byte aligned for 1-, 2- and 4-byte element types.
-FLAT_ALIGN = 16
+# Views into one allocation start at multiples of this many bytes. The
+# library needs 16-byte aligned tensors; a start that is not on a 64-byte
+# memory segment makes the first and last segment of every wave-wide access
+# shared with the neighbouring access, and each such segment then moves
+# twice (non-temporal accesses do not keep it in L2).
+FLAT_ALIGN_BYTES = 256
 
 
 def flat_views(sizes: Sequence[int], dtype, device, fill=0):
     """One contiguous allocation holding len(sizes) tensors, returned as 1-D
-    views (each starting at a multiple of FLAT_ALIGN elements). On MI355X one
+    views, each starting at a multiple of FLAT_ALIGN_BYTES. On MI355X one
     large buffer per role streams faster than many separate allocations."""
+    align = max(1, FLAT_ALIGN_BYTES // torch.tensor([], dtype=dtype).element_size())
     offsets, total = [], 0
     for k in sizes:
         offsets.append(total)
-        total += -(-int(k) // FLAT_ALIGN) * FLAT_ALIGN
+        total += -(-int(k) // align) * align
     buf = torch.full((max(total, 1),), fill, dtype=dtype, device=device)
     return [buf[o:o + int(k)] for o, k in zip(offsets, sizes)]
 
