@@ -357,6 +357,8 @@ def _kind_of(name: str):
         return ("copy_probe" if targs and targs[0] == "true" else "read_probe"), 0
     if fn == "k_rmw_probe":
         return "rmw_probe", PASS2_BYTES
+    if fn == "k_qp1_probe":
+        return "qp1_probe", QUANTIZE_PASS1_BYTES
     if fn == "k_scaled_v_pass1":  # also reads the FP16 second moment
         return "step_pass1", PASS1_BYTES + 2
     if fn == "k_scaled_v_pass2":
@@ -687,6 +689,17 @@ def main() -> int:
         M.profile_enable(False)
         n_p, ms_p = M.profile_read("rmw_probe")
         probe_ms = ms_p / n_p if n_p else None
+    # the fused quantize + pass 1's traffic without arithmetic, on the same
+    # buffers (it overwrites the gradient codes; the timed steps are done)
+    qp1_ms = None
+    if not args.no_profile and fused:
+        M.profile_enable(True)
+        for _ in range(5):
+            M.quantize_pass1_probe(st.grad_sets[0], st.grad_q, st.tl_m, st.tl_v, st.tl_w)
+        torch.cuda.synchronize()
+        M.profile_enable(False)
+        n_q, ms_q = M.profile_read("qp1_probe")
+        qp1_ms = ms_q / n_q if n_q else None
     # plain read and copy streams over the run's own binary32 gradient
     # buffers (4 bytes per parameter each; the timed steps are done, so the
     # second set may be overwritten)
@@ -758,6 +771,10 @@ def main() -> int:
             ceil["update_pass_mix"] = {"bytes": PASS2_BYTES * P, "ms": round(probe_ms, 4),
                                        "GB/s": round(PASS2_BYTES * P / (probe_ms * 1e-3) / 1e9, 1),
                                        "probe": "msamp_rmw_probe (read 6, write 5 B/p)"}
+        if qp1_ms:
+            ceil["quantize_pass1_mix"] = {"bytes": QUANTIZE_PASS1_BYTES * P, "ms": round(qp1_ms, 4),
+                                          "GB/s": round(QUANTIZE_PASS1_BYTES * P / (qp1_ms * 1e-3) / 1e9, 1),
+                                          "probe": "msamp_quantize_pass1_probe (read 5, write 1 B/p)"}
         roofline["ceilings"] = ceil
     opt_ms = sum(kernels[k]["avg_ms"] for k in ("step_pass1", "quantize_pass1", dom, "o3_pass3", "finalize")
                  if k in kernels)

@@ -40,7 +40,7 @@ __all__ = [
     # state helpers
     "new_meta", "allocate_state", "flat_views", "state_bytes_per_param",
     # measurement and test aids
-    "rmw_probe", "stream_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
+    "rmw_probe", "quantize_pass1_probe", "stream_probe", "codec_probe", "profile_enable", "profile_select", "profile_read", "release_cache",
     "unpin_captured_tables", "cache_stats",
 ]
 
@@ -57,7 +57,7 @@ PROBE_F16_TO_F32 = 5
 # kernel kinds of msamp_profile_read, in enum order
 KERNELS = ["amax", "quantize_fp8", "dequantize_fp8", "step_pass1", "o2_pass2", "o3_pass2",
            "o3_pass3", "finalize", "amax_finalize", "o2_delayed", "rmw_probe", "quantize_pass1",
-           "read_probe", "copy_probe"]
+           "read_probe", "copy_probe", "qp1_probe"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "libmsamp.so")
@@ -145,6 +145,8 @@ def lib():
         L.msamp_adamw_o3_step_phase3.argtypes = o3_args + [vp, vp]
         for f in ("o2_step_phase1", "o2_step_phase2", "o3_step_phase1", "o3_step_phase2", "o3_step_phase3"):
             getattr(L, "msamp_adamw_" + f).restype = st
+        L.msamp_quantize_pass1_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp]
+        L.msamp_quantize_pass1_probe.restype = st
         L.msamp_stream_probe.argtypes = [ctypes.c_int, vp, vp, i64, vp]
         L.msamp_stream_probe.restype = st
         L.msamp_rmw_probe.argtypes = [i32, vp, vp, vp, vp, vp, vp]
@@ -589,6 +591,23 @@ def rmw_probe(grad, exp_avg, exp_avg_sq, weight) -> None:
         return
     with torch.cuda.device(g.device):
         _check(lib().msamp_rmw_probe(g.n, g.numel, g.ptrs, m.ptrs, v.ptrs, w.ptrs, _stream(g.device)))
+
+
+def quantize_pass1_probe(grad_f32, grad, exp_avg, exp_avg_sq, weight) -> None:
+    """Measurement aid: the fused quantize + pass 1's traffic without its
+    arithmetic (msamp_quantize_pass1_probe); overwrites the gradient codes."""
+    x = _tl(grad_f32, "f32", "grad_f32")
+    g = _tl(grad, "u8", "grad")
+    m = _tl(exp_avg, "u8", "exp_avg")
+    v = _tl(exp_avg_sq, "f16", "exp_avg_sq")
+    w = _tl(weight, "f16", "weight")
+    for other, name in ((g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq"), (w, "weight")):
+        x.matches(other, name)
+    if x.n == 0:
+        return
+    with torch.cuda.device(x.device):
+        _check(lib().msamp_quantize_pass1_probe(x.n, x.numel, x.ptrs, g.ptrs, m.ptrs, v.ptrs, w.ptrs,
+                                                _stream(x.device)))
 
 
 def stream_probe(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> None:

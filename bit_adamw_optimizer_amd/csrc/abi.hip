@@ -868,6 +868,7 @@ const char* msamp_kernel_name(msamp_kernel_kind kind) {
     case MSAMP_KERNEL_QUANTIZE_PASS1: return "quantize_pass1";
     case MSAMP_KERNEL_READ_PROBE: return "read_probe";
     case MSAMP_KERNEL_COPY_PROBE: return "copy_probe";
+    case MSAMP_KERNEL_QP1_PROBE: return "qp1_probe";
     default: return "";
   }
 }
@@ -1225,6 +1226,30 @@ msamp_status msamp_cache_stats(int64_t* lists, int64_t* bytes, int64_t* pinned) 
     if (lists) *lists = (int64_t)c.count;
     if (bytes) *bytes = (int64_t)c.bytes;
     if (pinned) *pinned = np;
+    return MSAMP_OK;
+  });
+}
+
+msamp_status msamp_quantize_pass1_probe(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                        uint8_t* const* grad, uint8_t* const* exp_avg,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight, void* stream) {
+  return guarded([&]() -> msamp_status {
+    g_last_error.clear();
+    MSAMP_TRY(check_common(n, numel));
+    if (n == 0) return MSAMP_OK;
+    MSAMP_TRY(check_list(n, numel, (const void* const*)grad_f32, "grad_f32"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
+    MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
+    hipStream_t s = (hipStream_t)stream;
+    const void* const* roles[6] = {(const void* const*)grad,       (const void* const*)exp_avg,
+                                   (const void* const*)exp_avg_sq, (const void* const*)weight,
+                                   nullptr,                        (const void* const*)grad_f32};
+    Plan* p = nullptr;
+    std::unique_lock<std::mutex> lease;
+    MSAMP_TRY(get_plan(kPlanQuantizeO2, n, numel, roles, 6, true, s, &p, &lease));
+    MSAMP_LAUNCH(MSAMP_KERNEL_QP1_PROBE, s, launch_qp1_probe(p->desc, p->chunks, p->nchunks, s));
     return MSAMP_OK;
   });
 }

@@ -806,6 +806,44 @@ __global__ __launch_bounds__(kBlock) void k_rmw_probe(const TensorDesc* __restri
   }
 }
 
+// The fused quantize + pass 1's loads and stores without its arithmetic
+// (measurement aid): the same lanes, tiles and launch; reads the binary32
+// gradient (aux) and the first-moment codes (p1) and writes an unspecified
+// mix of them to the gradient codes (p0), 6 bytes per element.
+__global__ __launch_bounds__(kBlock) void k_qp1_probe(const TensorDesc* __restrict__ desc,
+                                                      const ChunkRef* __restrict__ chunks) {
+  const ChunkRange r = chunk_range(chunks, desc);
+  const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].aux);
+  GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(const_cast<void*>(desc[r.t].p0));
+  const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+    if (group4_base(tile, 3) + 4 <= r.end) {
+      u32x4 v[4];
+      uint32_t mw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = load_stream<u32x4>(x + group4_base(tile, j));
+        mw[j] = load_stream<uint32_t>(mq + group4_base(tile, j));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t c = v[j].x ^ v[j].y ^ v[j].z ^ v[j].w ^ mw[j];
+        asm volatile("" : "+v"(c));
+        store_stream<uint32_t>(q + group4_base(tile, j), c);
+      }
+    } else {
+      for (int j = 0; j < 4; ++j) {
+        const int64_t e = group4_base(tile, j);
+        for (int64_t i = e; i < e + 4 && i < r.end; ++i) {
+          uint32_t c = __float_as_uint(x[i]) ^ mq[i];
+          asm volatile("" : "+v"(c));
+          q[i] = (uint8_t)c;
+        }
+      }
+    }
+  }
+}
+
 // Plain streams over one buffer in 16-byte units (measurement aid): the
 // lanes of the amax kernel's FP32 layout (each wave instruction covers 1 KB
 // of consecutive memory, 16 KB per tile, 256 KB per workgroup), non-temporal
@@ -1090,6 +1128,12 @@ hipError_t launch_stream_probe(bool copy, const void* src, void* dst, int64_t by
     k_stream_probe<true><<<g, kBlock, 0, stream>>>((const u32x4*)src, (u32x4*)dst, units);
   else
     k_stream_probe<false><<<g, kBlock, 0, stream>>>((const u32x4*)src, (u32x4*)dst, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_qp1_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks, hipStream_t stream) {
+  if (nchunks <= 0) return hipSuccess;
+  k_qp1_probe<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
   return hipGetLastError();
 }
 

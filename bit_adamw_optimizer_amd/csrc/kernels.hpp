@@ -139,6 +139,9 @@ hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64
 hipError_t launch_step_finalize(int32_t n, uint32_t* amax_a, msamp_meta* meta_a,
                                 uint32_t* amax_b, msamp_meta* meta_b, float fmax_b,
                                 hipStream_t stream);
+// The fused quantize + pass 1's traffic without arithmetic, over a
+// quantizing-step plan (writes unspecified values to the gradient codes).
+hipError_t launch_qp1_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks, hipStream_t stream);
 // Measurement streams: read 'bytes' from src, or copy them to dst (bytes a
 // multiple of 16, 16-byte aligned pointers).
 hipError_t launch_stream_probe(bool copy, const void* src, void* dst, int64_t bytes, hipStream_t stream);

@@ -496,6 +496,20 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
                              uint16_t* const* weight, void* stream);
 
 /*
+ * msamp_quantize_pass1_probe -- MEASUREMENT AID, not part of the method:
+ * the loads and stores of the fused gradient quantize + pass 1 of
+ * msamp_quantize_adamw_o2_step without its arithmetic (same lanes, tiles and
+ * launch): reads grad_f32 and exp_avg, and writes UNSPECIFIED values to the
+ * gradient codes 'grad' (6 bytes per element). Its rate on the caller's own
+ * buffers is the ceiling the memory system gives that pass there. Arguments
+ * and errors as msamp_quantize_adamw_o2_step (the lists must be the ones a
+ * quantizing step uses, with exp_avg_sq and weight); no meta is touched.
+ */
+msamp_status msamp_quantize_pass1_probe(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                        uint8_t* const* grad, uint8_t* const* exp_avg,
+                                        uint16_t* const* exp_avg_sq, uint16_t* const* weight, void* stream);
+
+/*
  * msamp_stream_probe -- MEASUREMENT AID, not part of the method: a plain
  * stream at the launch shape of the library's kernels (16-byte accesses,
  * each wave instruction on 1 KB of consecutive memory, 256 KB per
@@ -527,7 +541,8 @@ typedef enum {
   MSAMP_KERNEL_QUANTIZE_PASS1 = 11, /* gradient quantize fused with pass 1 */
   MSAMP_KERNEL_READ_PROBE = 12, /* msamp_stream_probe, MSAMP_STREAM_READ */
   MSAMP_KERNEL_COPY_PROBE = 13, /* msamp_stream_probe, MSAMP_STREAM_COPY */
-  MSAMP_KERNEL_COUNT = 14
+  MSAMP_KERNEL_QP1_PROBE = 14,  /* msamp_quantize_pass1_probe (measurement aid) */
+  MSAMP_KERNEL_COUNT = 15
 } msamp_kernel_kind;
 
 /* on != 0 starts recording (and discards earlier records; the events for

@@ -41,7 +41,7 @@ def test_bench_json_contract():
     assert rf["kernel"] == "o2_pass2" and 0 < rf["frac"] < 1
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert 0 < rf["same_buffers_ceiling"]["frac"] < 1.2
-    assert set(rf["ceilings"]) == {"read", "copy", "update_pass_mix"}
+    assert set(rf["ceilings"]) == {"read", "copy", "update_pass_mix", "quantize_pass1_mix"}
     assert all(c["GB/s"] > 0 for c in rf["ceilings"].values())
     # default: the gradient quantize runs fused with pass 1 (21 bytes per parameter)
     assert d["config"]["fused_quantize"] is True and d["bytes_per_param"] == 21

@@ -75,3 +75,19 @@ def test_fused_equals_quantize_then_step_byte_for_byte(wl):
         for i, (x, y) in enumerate(zip(a, b)):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (wl, s, i)
     log("%s: fused and two-call paths identical over 4 steps" % wl)
+
+
+def test_quantize_pass1_probe_touches_only_the_gradient_codes():
+    """The measurement probe of the fused pass reads the binary32 gradient
+    and the first-moment codes and writes only the gradient codes."""
+    w = W.make("tiny_stress")
+    gs = GpuState(w, "cuda")
+    gs.fill_grads(1)
+    gs.step(1)
+    torch.cuda.synchronize()
+    before = [x.clone() for x in gs.grad_f32 + gs.exp_avg + gs.exp_avg_sq + gs.weights]
+    for _ in range(2):
+        M.quantize_pass1_probe(gs.tl_g32, gs.tl_gq, gs.tl_m, gs.tl_v, gs.tl_w)
+    torch.cuda.synchronize()
+    after = gs.grad_f32 + gs.exp_avg + gs.exp_avg_sq + gs.weights
+    assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(before, after))
