@@ -36,9 +36,10 @@ __device__ __forceinline__ const GLOBAL T* global_ptr(const void* p) {
   return (const GLOBAL T*)p;
 }
 
-// Non-temporal loads: for streams read once that need not stay in any
-// cache (they are not allocated in the memory-side cache either, so they do
-// not evict data that is about to be read again).
+// Non-temporal loads: for streams that need not stay in any cache until
+// they are read again (read once, or read again only after far more data has
+// gone through the caches), so that they do not evict data that is about to
+// be read again.
 template <typename T>
 __device__ __forceinline__ T load_stream(const GLOBAL void* p) {
   return __builtin_nontemporal_load((const GLOBAL T*)p);
