@@ -127,7 +127,7 @@ class State:
         self.adam = adam
         self.delayed = delayed
         self.scaled_v = scaled_v
-        self.fused = fused  # gradient quantize fused with pass 1 of the AdamW step
+        self.fused = fused  # gradient quantize fused with pass 1 of the AdamW or Adam step
         self.exp_avg_sq_meta = M.new_meta(w.n, device) if scaled_v else None
         # every role lives in one allocation (views per tensor). Lists of many
         # tensors without per-tensor factors draw their inputs over the whole
@@ -181,6 +181,16 @@ class State:
 
         w = self.w
         M.amax(g32, self.grad_meta)
+        if self.fused and w.level == "O2":
+            M.quantize_adamw_o2_step_devconst(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
+                                              self.exp_avg_meta, self.tl_v, self.tl_w, self.consts,
+                                              adam=self.adam)
+            return
+        if self.fused:
+            M.quantize_adamw_o3_step_devconst(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
+                                              self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
+                                              self.weight_fp8_meta, self.consts, adam=self.adam)
+            return
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2":
             M.adamw_o2_step_devconst(self.grad_q, w.grad_fmt, self.grad_meta, self.tl_m,
@@ -215,11 +225,12 @@ class State:
         if self.fused:
             if w.level == "O2":
                 M.quantize_adamw_o2_step(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
-                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, adam=self.adam,
+                                         **w.hparams())
             else:
                 M.quantize_adamw_o3_step(g32, w.grad_fmt, self.grad_meta, self.grad_q, self.tl_m,
                                          self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
-                                         self.weight_fp8_meta, step=step, **w.hparams())
+                                         self.weight_fp8_meta, step=step, adam=self.adam, **w.hparams())
             return
         M.quantize_fp8(g32, w.grad_fmt, self.grad_meta, self.grad_q)
         if w.level == "O2" and self.scaled_v:
@@ -351,8 +362,9 @@ def _kind_of(name: str):
         return ("o3_pass2" if len(targs) > 1 and targs[1] == "true" else "o2_pass2"), PASS2_BYTES
     if fn == "k_o3_pass3":
         return "o3_pass3", PASS3_BYTES
-    if fn == "k_quantize_pass1":
-        return "quantize_pass1", QUANTIZE_PASS1_BYTES
+    if fn == "k_quantize_pass1":  # <grad format, coupled>
+        coupled = len(targs) > 1 and targs[1] == "true"
+        return "quantize_pass1", QUANTIZE_PASS1_BYTES + (2 if coupled else 0)
     if fn == "k_stream_probe":  # <copy>: measurement streams (bytes are not per parameter)
         return ("copy_probe" if targs and targs[0] == "true" else "read_probe"), 0
     if fn == "k_rmw_probe":
@@ -621,7 +633,7 @@ def main() -> int:
     if (delayed or scaled_v) and w.level != "O2":
         print("the %s ablation exists for the O2 layout only" % args.optimizer, file=sys.stderr)
         return 2
-    fused = not (args.separate_quantize or adam or delayed or scaled_v or args.graph)
+    fused = not (args.separate_quantize or delayed or scaled_v)
     st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, fused=fused)
     if args.graph:
         if delayed or scaled_v:
@@ -692,7 +704,7 @@ def main() -> int:
     # the fused quantize + pass 1's traffic without arithmetic, on the same
     # buffers (it overwrites the gradient codes; the timed steps are done)
     qp1_ms = None
-    if not args.no_profile and fused:
+    if not args.no_profile and fused and not adam:
         M.profile_enable(True)
         for _ in range(5):
             M.quantize_pass1_probe(st.grad_sets[0], st.grad_q, st.tl_m, st.tl_v, st.tl_w)
@@ -726,10 +738,12 @@ def main() -> int:
     # (and so does the scaled-v ablation's, for its amax(v1))
     pass1_bytes = PASS1_BYTES + (2 if adam or scaled_v else 0)
     step_bytes = (0 if delayed else pass1_bytes) + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+    qp1_bytes = QUANTIZE_PASS1_BYTES + (2 if adam else 0)
     if fused:
         # the quantize writes the codes and pass 1 takes them from registers:
-        # one launch reads the f32 gradient and the first moment, writes the codes
-        step_bytes = QUANTIZE_PASS1_BYTES + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
+        # one launch reads the f32 gradient and the first moment (and, for
+        # Adam, the weight), and writes the codes
+        step_bytes = qp1_bytes + PASS2_BYTES + (PASS3_BYTES if w.level == "O3" else 0)
         path_bytes = GRAD_AMAX_BYTES + step_bytes
     else:
         path_bytes = GRAD_AMAX_BYTES + GRAD_QUANTIZE_BYTES + step_bytes
@@ -737,7 +751,7 @@ def main() -> int:
 
     per_kernel_bytes = {"amax": GRAD_AMAX_BYTES, "quantize_fp8": GRAD_QUANTIZE_BYTES,
                         "step_pass1": pass1_bytes, "o2_pass2": PASS2_BYTES, "o3_pass2": PASS2_BYTES,
-                        "quantize_pass1": QUANTIZE_PASS1_BYTES,
+                        "quantize_pass1": qp1_bytes,
                         "o3_pass3": PASS3_BYTES, "o2_delayed": PASS2_BYTES}
     breakdown = {}
     for k, d in kernels.items():

@@ -35,6 +35,7 @@ __all__ = [
     "adamw_o2_step", "adamw_o3_step", "adam_o2_step", "adam_o3_step",
     "step_constants", "adamw_o2_step_devconst", "adamw_o3_step_devconst", "adamw_step_phase",
     "adamw_o2_step_noalloc", "quantize_adamw_o2_step", "quantize_adamw_o3_step",
+    "quantize_adamw_o2_step_devconst", "quantize_adamw_o3_step_devconst",
     # ablations
     "adamw_o2_step_delayed", "adamw_o2_step_scaled_v",
     # state helpers
@@ -124,6 +125,16 @@ def lib():
         L.msamp_quantize_adamw_o3_step.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp,
                                                    vp, ctypes.POINTER(_HParams), i64, vp]
         L.msamp_quantize_adamw_o3_step.restype = st
+        L.msamp_quantize_adam_o2_step.argtypes = L.msamp_quantize_adamw_o2_step.argtypes
+        L.msamp_quantize_adam_o2_step.restype = st
+        L.msamp_quantize_adam_o3_step.argtypes = L.msamp_quantize_adamw_o3_step.argtypes
+        L.msamp_quantize_adam_o3_step.restype = st
+        L.msamp_quantize_adamw_o2_step_devconst.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                            vp, ctypes.c_int, vp]
+        L.msamp_quantize_adamw_o2_step_devconst.restype = st
+        L.msamp_quantize_adamw_o3_step_devconst.argtypes = [i32, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                                            vp, vp, vp, ctypes.c_int, vp]
+        L.msamp_quantize_adamw_o3_step_devconst.restype = st
         L.msamp_adamw_o2_step_noalloc.argtypes = L.msamp_adamw_o2_step.argtypes
         L.msamp_adamw_o2_step_noalloc.restype = st
         L.msamp_adam_o2_step.argtypes = L.msamp_adamw_o2_step.argtypes
@@ -370,23 +381,49 @@ def adamw_o3_step(grad, grad_fmt: int, grad_meta, exp_avg, exp_avg_meta, exp_avg
 
 def quantize_adamw_o2_step(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq,
                            weight, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
-                           step: int) -> None:
-    """Gradient quantize fused with the O2 AdamW step (see include/msamp.h):
-    grad_meta must hold the gradient amax; grad receives the FP8 codes."""
-    _quantize_step("O2", grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight,
-                   None, None, _hp(lr, betas, eps, weight_decay), step)
+                           step: int, adam: bool = False) -> None:
+    """Gradient quantize fused with the O2 AdamW step (Adam with adam=True;
+    see include/msamp.h): grad_meta must hold the gradient amax; grad
+    receives the FP8 codes."""
+    hp = _hp(lr, betas, eps, weight_decay)
+    _quantize_step("O2", "msamp_quantize_adam_o2_step" if adam else "msamp_quantize_adamw_o2_step",
+                   grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight, None, None,
+                   (ctypes.byref(hp), int(step)))
 
 
 def quantize_adamw_o3_step(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq,
                            master, weight_fp8, weight_fp8_meta, *, lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
-                           weight_decay=0.01, step: int) -> None:
-    """Gradient quantize fused with the O3 AdamW step (see include/msamp.h)."""
-    _quantize_step("O3", grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, master,
-                   weight_fp8, weight_fp8_meta, _hp(lr, betas, eps, weight_decay), step)
+                           weight_decay=0.01, step: int, adam: bool = False) -> None:
+    """Gradient quantize fused with the O3 AdamW step (Adam with adam=True;
+    see include/msamp.h)."""
+    hp = _hp(lr, betas, eps, weight_decay)
+    _quantize_step("O3", "msamp_quantize_adam_o3_step" if adam else "msamp_quantize_adamw_o3_step",
+                   grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, master, weight_fp8,
+                   weight_fp8_meta, (ctypes.byref(hp), int(step)))
 
 
-def _quantize_step(level, grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight,
-                   weight_fp8, weight_fp8_meta, hp, step) -> None:
+def quantize_adamw_o2_step_devconst(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta,
+                                    exp_avg_sq, weight, consts: torch.Tensor, adam: bool = False) -> None:
+    """msamp_quantize_adamw_o2_step_devconst: the fused O2 step with the
+    step's constants read from 'consts' (see step_constants) when it runs."""
+    g = _tl(grad_f32, "f32", "grad_f32")
+    _quantize_step("O2", "msamp_quantize_adamw_o2_step_devconst", grad_f32, grad_fmt, grad_meta, grad, exp_avg,
+                   exp_avg_meta, exp_avg_sq, weight, None, None,
+                   (_consts_ptr(consts, g.device), 1 if adam else 0))
+
+
+def quantize_adamw_o3_step_devconst(grad_f32, grad_fmt: int, grad_meta, grad, exp_avg, exp_avg_meta,
+                                    exp_avg_sq, master, weight_fp8, weight_fp8_meta, consts: torch.Tensor,
+                                    adam: bool = False) -> None:
+    """msamp_quantize_adamw_o3_step_devconst (see quantize_adamw_o2_step_devconst)."""
+    g = _tl(grad_f32, "f32", "grad_f32")
+    _quantize_step("O3", "msamp_quantize_adamw_o3_step_devconst", grad_f32, grad_fmt, grad_meta, grad, exp_avg,
+                   exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta,
+                   (_consts_ptr(consts, g.device), 1 if adam else 0))
+
+
+def _quantize_step(level, entry, grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_meta, exp_avg_sq, weight,
+                   weight_fp8, weight_fp8_meta, tail) -> None:
     x = _tl(grad_f32, "f32", "grad_f32")
     g = _tl(grad, "u8", "grad")
     m = _tl(exp_avg, "u8", "exp_avg")
@@ -402,17 +439,11 @@ def _quantize_step(level, grad_f32, grad_fmt, grad_meta, grad, exp_avg, exp_avg_
     if x.n == 0:
         return
     with torch.cuda.device(x.device):
-        gm = _meta_ptr(grad_meta, x.n, x.device, "grad_meta")
-        mm = _meta_ptr(exp_avg_meta, x.n, x.device, "exp_avg_meta")
-        if level == "O2":
-            _check(lib().msamp_quantize_adamw_o2_step(x.n, x.numel, x.ptrs, int(grad_fmt), gm, g.ptrs, m.ptrs,
-                                                      mm, v.ptrs, w.ptrs, ctypes.byref(hp), int(step),
-                                                      _stream(x.device)))
-        else:
-            _check(lib().msamp_quantize_adamw_o3_step(
-                x.n, x.numel, x.ptrs, int(grad_fmt), gm, g.ptrs, m.ptrs, mm, v.ptrs, w.ptrs, w8.ptrs,
-                _meta_ptr(weight_fp8_meta, x.n, x.device, "weight_fp8_meta"), ctypes.byref(hp), int(step),
-                _stream(x.device)))
+        args = [x.n, x.numel, x.ptrs, int(grad_fmt), _meta_ptr(grad_meta, x.n, x.device, "grad_meta"), g.ptrs,
+                m.ptrs, _meta_ptr(exp_avg_meta, x.n, x.device, "exp_avg_meta"), v.ptrs, w.ptrs]
+        if level == "O3":
+            args += [w8.ptrs, _meta_ptr(weight_fp8_meta, x.n, x.device, "weight_fp8_meta")]
+        _check(getattr(lib(), entry)(*args, *tail, _stream(x.device)))
 
 
 def step_constants(*, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step: int,

@@ -514,17 +514,22 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
 
 // Gradient quantize + AdamW step (O2 or O3) with the quantize fused into
 // pass 1; the rest is the step's sequence.
-msamp_status quantize_step_impl(bool o3, int32_t n, const int64_t* numel, const float* const* grad_f32,
-                                int grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
-                                uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel,
+                                const float* const* grad_f32, int grad_fmt, msamp_meta* grad_meta,
+                                uint8_t* const* grad, uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
                                 uint16_t* const* exp_avg_sq, uint16_t* const* weight,
                                 uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
-                                const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr) {
+                                const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr,
+                                const StepConsts* kdev = nullptr) {
   g_last_error.clear();
   MSAMP_TRY(check_common(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
-  MSAMP_TRY(check_hparams(hp, step));
+  if (kdev == nullptr) {
+    MSAMP_TRY(check_hparams(hp, step));
+  } else if (((uintptr_t)kdev & 3u) != 0) {
+    return fail(MSAMP_E_MISALIGNED, "consts is not 4-byte aligned");
+  }
   MSAMP_TRY(check_list(n, numel, (const void* const*)grad_f32, "grad_f32"));
   MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
                              weight_fp8, weight_fp8_meta));
@@ -536,14 +541,14 @@ msamp_status quantize_step_impl(bool o3, int32_t n, const int64_t* numel, const 
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
   MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, 6, true, s, &p, &lease));
-  const StepConsts k = make_consts(hp, step, false);
+  const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
   MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE_PASS1, s,
-               launch_quantize_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
-                                     p->scratch_a, k, s));
+               launch_quantize_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
+                                     p->scratch_a, k, s, kdev));
   const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
-               launch_step_pass2(grad_fmt, o3, false, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, nullptr,
+               launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev,
                                  o3 ? MetaFold{} : fold));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
@@ -1155,8 +1160,33 @@ msamp_status msamp_quantize_adamw_o2_step(int32_t n, const int64_t* numel, const
                                           uint16_t* const* weight, const msamp_adamw_hparams* hp,
                                           int64_t step, void* stream) {
   return guarded([&]() {
-    return quantize_step_impl(false, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+    return quantize_step_impl(false, false, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
                               exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
+  });
+}
+
+msamp_status msamp_quantize_adam_o2_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                         msamp_fp8_format grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return quantize_step_impl(false, true, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, hp, step, stream);
+  });
+}
+
+msamp_status msamp_quantize_adamw_o2_step_devconst(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                                   msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                                   uint8_t* const* grad, uint8_t* const* exp_avg,
+                                                   msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                                   uint16_t* const* weight, const msamp_step_constants* consts,
+                                                   int coupled, void* stream) {
+  return guarded([&]() -> msamp_status {
+    if (consts == nullptr) return fail(MSAMP_E_INVALID_ARG, "consts is NULL");
+    return quantize_step_impl(false, coupled != 0, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, weight, nullptr, nullptr, nullptr, 0, stream,
+                              (const StepConsts*)consts);
   });
 }
 
@@ -1168,9 +1198,37 @@ msamp_status msamp_quantize_adamw_o3_step(int32_t n, const int64_t* numel, const
                                           msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp,
                                           int64_t step, void* stream) {
   return guarded([&]() {
-    return quantize_step_impl(true, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+    return quantize_step_impl(true, false, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
                               exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step,
                               stream);
+  });
+}
+
+msamp_status msamp_quantize_adam_o3_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                         msamp_fp8_format grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                         uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream) {
+  return guarded([&]() {
+    return quantize_step_impl(true, true, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, hp, step,
+                              stream);
+  });
+}
+
+msamp_status msamp_quantize_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                                   msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                                   uint8_t* const* grad, uint8_t* const* exp_avg,
+                                                   msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                                   uint16_t* const* master, uint8_t* const* weight_fp8,
+                                                   msamp_meta* weight_fp8_meta, const msamp_step_constants* consts,
+                                                   int coupled, void* stream) {
+  return guarded([&]() -> msamp_status {
+    if (consts == nullptr) return fail(MSAMP_E_INVALID_ARG, "consts is NULL");
+    return quantize_step_impl(true, coupled != 0, n, numel, grad_f32, (int)grad_fmt, grad_meta, grad, exp_avg,
+                              exp_avg_meta, exp_avg_sq, master, weight_fp8, weight_fp8_meta, nullptr, 0, stream,
+                              (const StepConsts*)consts);
   });
 }
 

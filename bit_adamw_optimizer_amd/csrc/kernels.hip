@@ -368,17 +368,46 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   block_max_into(mx, &amax_m[r.t]);
 }
 
-// Gradient quantize fused with pass 1 (AdamW, O2 and O3). The codes are
+// Gradient quantize fused with pass 1 (O2 and O3; AdamW, or Adam when
+// COUPLED, which also reads the FP16 weight for its L2 term). The codes are
 // computed exactly as k_quantize computes them (same scale, same NaN-aware
 // saturating encode), stored, and decoded from registers for pass 1, so they
 // are not read back from memory. Every stream uses the FP32 lane layout
-// (4-element groups): 16-byte gradient loads, 4-byte code loads and stores.
-template <int GF>
+// (4-element groups): 16-byte gradient loads, 4-byte code loads and stores,
+// 8-byte weight loads. The step constants come by value (kv), or from device
+// memory when kdev is not null (a captured launch replayed for later steps).
+template <int GF, bool COUPLED>
+__device__ __forceinline__ uint32_t qp1_group(const StepConsts& k, const u32x4& v, uint32_t mw, const u32x2& wv,
+                                              float s, float gsi, float msi, uint32_t* code) {
+  const float f[4] = {__uint_as_float(v.x) * s, __uint_as_float(v.y) * s, __uint_as_float(v.z) * s,
+                      __uint_as_float(v.w) * s};
+  const uint32_t c = enc4_nan<GF>(f);
+  *code = c;
+  float g[4], m[4], w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  dec4<GF>(c, g);
+  dec4<kE4M3>(mw, m);
+  if (COUPLED) {
+    const f32x2 a = h2_to_f2(wv.x), b = h2_to_f2(wv.y);
+    w[0] = a.x;
+    w[1] = a.y;
+    w[2] = b.x;
+    w[3] = b.y;
+  }
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    mx = umax(mx, abs_bits(first_moment(k, effective_grad<COUPLED>(k, g[i] * gsi, w[i]), m[i] * msi)));
+  return mx;
+}
+
+template <int GF, bool COUPLED>
 __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __restrict__ desc,
                                                            const ChunkRef* __restrict__ chunks,
                                                            msamp_meta* __restrict__ gmeta,
                                                            const msamp_meta* __restrict__ mmeta,
-                                                           uint32_t* __restrict__ amax_m, StepConsts k) {
+                                                           uint32_t* __restrict__ amax_m, StepConsts kv,
+                                                           const StepConsts* __restrict__ kdev) {
+  const StepConsts k = kdev != nullptr ? *kdev : kv;
   const ChunkRange r = chunk_range(chunks, desc);
   const float s = scale_rule(gmeta[r.t].amax, Fp8Traits<GF>::kMax);
   const float gsi = 1.0f / s;
@@ -392,47 +421,41 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __r
   // p0 is the step's (read-only) gradient role; this kernel produces it
   GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(const_cast<void*>(desc[r.t].p0));
   const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
+  // Adam's pass 1 reads the weight; pass 2 reads it again soon after
+  const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
+  const u32x2 nowt = {0u, 0u};
   uint32_t mx = 0u;
   for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
     if (group4_base(tile, 3) + 4 <= r.end) {
       u32x4 v[4];
       uint32_t mw[4];
+      u32x2 wv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[j] = load_stream<u32x4>(x + group4_base(tile, j));
         mw[j] = load_stream<uint32_t>(mq + group4_base(tile, j));
+        wv[j] = COUPLED ? load<u32x2>(wh + group4_base(tile, j)) : nowt;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float f[4] = {__uint_as_float(v[j].x) * s, __uint_as_float(v[j].y) * s,
-                            __uint_as_float(v[j].z) * s, __uint_as_float(v[j].w) * s};
-        const uint32_t c = enc4_nan<GF>(f);
+        uint32_t c;
+        mx = umax(mx, qp1_group<GF, COUPLED>(k, v[j], mw[j], wv[j], s, gsi, msi, &c));
         store_stream<uint32_t>(q + group4_base(tile, j), c);
-        float g[4], m[4];
-        dec4<GF>(c, g);
-        dec4<kE4M3>(mw[j], m);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = umax(mx, abs_bits(first_moment(k, g[i] * gsi, m[i] * msi)));
       }
     } else {
       for (int j = 0; j < 4; ++j) {
         const int64_t e = group4_base(tile, j);
         if (e + 4 <= r.end) {
-          const u32x4 v = load_stream<u32x4>(x + e);
-          const float f[4] = {__uint_as_float(v.x) * s, __uint_as_float(v.y) * s, __uint_as_float(v.z) * s,
-                              __uint_as_float(v.w) * s};
-          const uint32_t c = enc4_nan<GF>(f);
+          uint32_t c;
+          mx = umax(mx, qp1_group<GF, COUPLED>(k, load_stream<u32x4>(x + e), load_stream<uint32_t>(mq + e),
+                                               COUPLED ? load<u32x2>(wh + e) : nowt, s, gsi, msi, &c));
           store_stream<uint32_t>(q + e, c);
-          float g[4], m[4];
-          dec4<GF>(c, g);
-          dec4<kE4M3>(load_stream<uint32_t>(mq + e), m);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = umax(mx, abs_bits(first_moment(k, g[i] * gsi, m[i] * msi)));
         } else {
           for (int64_t i = e; i < r.end; ++i) {
             const uint32_t c = enc1_nan<GF>(x[i] * s);
             q[i] = (uint8_t)c;
-            mx = umax(mx, abs_bits(first_moment(k, dec1<GF>((uint8_t)c) * gsi, dec1<kE4M3>(mq[i]) * msi)));
+            const float ge = effective_grad<COUPLED>(k, dec1<GF>((uint8_t)c) * gsi, COUPLED ? h_to_f(wh[i]) : 0.0f);
+            mx = umax(mx, abs_bits(first_moment(k, ge, dec1<kE4M3>(mq[i]) * msi)));
           }
         }
       }
@@ -971,14 +994,22 @@ static void pass1_launch(unsigned g, hipStream_t stream, const TensorDesc* desc,
   k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
 }
 
-hipError_t launch_quantize_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                                 msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
-                                 const StepConsts& k, hipStream_t stream) {
+hipError_t launch_quantize_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                                 const StepConsts& k, hipStream_t stream, const StepConsts* kdev) {
   if (nchunks <= 0) return hipSuccess;
-  if (gfmt == kE4M3)
-    k_quantize_pass1<kE4M3><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
-  else
-    k_quantize_pass1<kE5M2><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k);
+  const unsigned g = grid_of(nchunks);
+  if (gfmt == kE4M3) {
+    if (coupled)
+      k_quantize_pass1<kE4M3, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else
+      k_quantize_pass1<kE4M3, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  } else {
+    if (coupled)
+      k_quantize_pass1<kE5M2, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else
+      k_quantize_pass1<kE5M2, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  }
   return hipGetLastError();
 }
 

@@ -96,12 +96,13 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
                              int64_t nchunks, const msamp_meta* meta, hipStream_t stream);
 // 'coupled' selects Adam (L2 term wd*w added to the gradient before the
 // moments); otherwise AdamW.
-// Fused gradient quantize + AdamW pass 1: q = enc(x * s) into p0 (s from
+// Fused gradient quantize + pass 1: q = enc(x * s) into p0 (s from
 // gmeta.amax; chunk 0 writes gmeta.scale / .scale_inv) and the pass-1 amax of
-// the new first moment from the codes in registers.
-hipError_t launch_quantize_pass1(int gfmt, const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                                 msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
-                                 const StepConsts& k, hipStream_t stream);
+// the new first moment from the codes in registers ('coupled': Adam, which
+// also reads the weight p3). Constants by value, or from kdev when not null.
+hipError_t launch_quantize_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
+                                 int64_t nchunks, msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                                 const StepConsts& k, hipStream_t stream, const StepConsts* kdev = nullptr);
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream,

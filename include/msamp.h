@@ -296,6 +296,22 @@ msamp_status msamp_quantize_adamw_o3_step(int32_t n, const int64_t* numel, const
                                           msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp,
                                           int64_t step, void* stream);
 
+/* msamp_quantize_adam_o2_step / msamp_quantize_adam_o3_step -- the same for
+ * torch.optim.Adam (coupled L2, see msamp_adam_o2_step): the fused pass also
+ * reads the weight (O2) or master (O3), 8 bytes per element, 19 (O2) or 22
+ * (O3) bytes per element in all against 20 / 23 for the two calls. */
+msamp_status msamp_quantize_adam_o2_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                         msamp_fp8_format grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream);
+msamp_status msamp_quantize_adam_o3_step(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                         msamp_fp8_format grad_fmt, msamp_meta* grad_meta, uint8_t* const* grad,
+                                         uint8_t* const* exp_avg, msamp_meta* exp_avg_meta,
+                                         uint16_t* const* exp_avg_sq, uint16_t* const* master,
+                                         uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
+                                         const msamp_adamw_hparams* hp, int64_t step, void* stream);
+
 /*
  * msamp_adam_o2_step / msamp_adam_o3_step -- the same steps for
  * torch.optim.Adam, the other optimizer the MS-AMP README recognizes ([RD]
@@ -388,6 +404,24 @@ msamp_status msamp_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const
                                           uint8_t* const* weight_fp8, msamp_meta* weight_fp8_meta,
                                           const msamp_step_constants* consts, int coupled,
                                           void* stream);
+
+/* The quantizing steps (msamp_quantize_adamw_o2_step / _o3_step, and the
+ * Adam ones with coupled = 1) with the constants read from consts (device,
+ * 4-byte aligned, one record) when the kernels run, as above: the gradient
+ * amax, this call and the constants' copy can be captured and replayed. */
+msamp_status msamp_quantize_adamw_o2_step_devconst(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                                   msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                                   uint8_t* const* grad, uint8_t* const* exp_avg,
+                                                   msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                                   uint16_t* const* weight, const msamp_step_constants* consts,
+                                                   int coupled, void* stream);
+msamp_status msamp_quantize_adamw_o3_step_devconst(int32_t n, const int64_t* numel, const float* const* grad_f32,
+                                                   msamp_fp8_format grad_fmt, msamp_meta* grad_meta,
+                                                   uint8_t* const* grad, uint8_t* const* exp_avg,
+                                                   msamp_meta* exp_avg_meta, uint16_t* const* exp_avg_sq,
+                                                   uint16_t* const* master, uint8_t* const* weight_fp8,
+                                                   msamp_meta* weight_fp8_meta, const msamp_step_constants* consts,
+                                                   int coupled, void* stream);
 
 /*
  * Split-phase steps, for a flat intra-tensor partition of the parameters

@@ -83,7 +83,7 @@ class GpuState:
                  scaled_v: bool = False, flat: bool = False, fused: bool = False):
         self.w = w
         self.device = device
-        self.fused = fused  # gradient quantize fused with pass 1 (AdamW only)
+        self.fused = fused  # gradient quantize fused with pass 1 (AdamW or Adam)
         self.adam = adam  # Adam (coupled L2) instead of AdamW
         self.delayed = delayed  # one-pass delayed-scaling ablation (O2 AdamW)
         self.scaled_v = scaled_v  # scaled-FP16-v ablation (O2 AdamW)
@@ -121,14 +121,15 @@ class GpuState:
         w = self.w
         M.amax(self.tl_g32, self.grad_meta)
         if self.fused:
-            assert not (self.adam or self.delayed or self.scaled_v)
+            assert not (self.delayed or self.scaled_v)
             if w.level == "O2":
                 M.quantize_adamw_o2_step(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq, self.tl_m,
-                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, **w.hparams())
+                                         self.exp_avg_meta, self.tl_v, self.tl_w, step=step, adam=self.adam,
+                                         **w.hparams())
             else:
                 M.quantize_adamw_o3_step(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq, self.tl_m,
                                          self.exp_avg_meta, self.tl_v, self.tl_w, self.tl_w8,
-                                         self.weight_fp8_meta, step=step, **w.hparams())
+                                         self.weight_fp8_meta, step=step, adam=self.adam, **w.hparams())
             return
         M.quantize_fp8(self.tl_g32, w.grad_fmt, self.grad_meta, self.tl_gq)
         if w.level == "O2" and self.scaled_v:

@@ -27,6 +27,8 @@ def test_kernel_names_map_to_kinds_and_bytes():
         "k_step_pass2<0, true, true, false>" + args: ("o3_pass2", 11),
         "k_step_pass2<1, false, false, true>" + args: ("o2_delayed", 11),
         "k_o3_pass3" + args: ("o3_pass3", 3),
+        "k_quantize_pass1<0, false>" + args: ("quantize_pass1", 6),
+        "k_quantize_pass1<1, true>" + args: ("quantize_pass1", 8),
         "k_rmw_probe" + args: ("rmw_probe", 11),
         "k_scaled_v_pass1<0>" + args: ("step_pass1", 4),
         "k_scaled_v_pass2<0>" + args: ("o2_pass2", 11),

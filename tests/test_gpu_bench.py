@@ -59,5 +59,16 @@ def test_bench_separate_quantize():
 
 
 def test_bench_graph_mode():
+    """Graph replay of amax + the quantizing device-constants step."""
     d = _run("--graph")
     assert d["config"]["graph"] is True and d["value"] > 0
+    assert d["config"]["fused_quantize"] is True and d["bytes_per_param"] == 21
+
+
+def test_bench_adam_fused():
+    """Adam's fused pass also reads the FP16 weight for the L2 term: 23 bytes
+    per parameter; the pass-1 probe (which has no weight read) is not run."""
+    d = _run("--optimizer", "adam")
+    assert d["config"]["fused_quantize"] is True and d["bytes_per_param"] == 23
+    assert set(d["kernels"]) >= {"amax", "quantize_pass1", "o2_pass2"}
+    assert "quantize_pass1_mix" not in d["roofline"]["ceilings"]

@@ -1,5 +1,6 @@
-"""The gradient quantize fused with pass 1 of the AdamW step
-(msamp_quantize_adamw_o2_step / _o3_step) against the oracle's unfused
+"""The gradient quantize fused with pass 1 of the AdamW and Adam steps
+(msamp_quantize_adamw_o2_step / _o3_step, msamp_quantize_adam_o2_step /
+_o3_step) against the oracle's unfused
 sequence (quantize, then the step: MS-AMP "Optimization Level" page, sections
 O2 and O3), and byte for byte against the library's own two calls
 (msamp_quantize_fp8 then msamp_adamw_o2_step / _o3_step)."""
@@ -31,6 +32,18 @@ def test_fused_quantize_step_matches_the_oracle(wl):
         assert list(mm[t, :3]) == [0.0, 1.0, 1.0]
 
 
+@pytest.mark.parametrize("wl", ["tiny_llama", "tiny_llama_o3", "tiny_stress"])
+def test_fused_adam_matches_the_oracle(wl):
+    """Adam (the decay folded into the gradient before the moments) through
+    the fused entry points."""
+    w = W.make(wl)
+    w.weight_decay = 0.1
+    log("%s %s fused adam, %d tensors, %d params" % (wl, w.level, w.n, w.params))
+    stats, _, _ = run_parity(w, 8 if wl != "tiny_stress" else 5, adam=True, fused=True)
+    _report(wl + " fused adam", stats)
+    assert_bar(stats)
+
+
 def test_fused_ragged_sizes():
     """Sizes around the 4-element group, the 4096-element tile and the
     65536-element chunk, including empty tensors."""
@@ -51,16 +64,19 @@ def _snapshot(gs, level):
     return [x.clone() for x in parts]
 
 
-@pytest.mark.parametrize("wl", ["tiny_stress", "tiny_llama_o3"])
-def test_fused_equals_quantize_then_step_byte_for_byte(wl):
+@pytest.mark.parametrize("wl,adam", [("tiny_stress", False), ("tiny_llama_o3", False), ("tiny_stress", True),
+                                     ("tiny_llama_o3", True)])
+def test_fused_equals_quantize_then_step_byte_for_byte(wl, adam):
     """Every output of the fused call, gradient codes and scales included,
     equals the two calls' outputs, step after step; step 3 plants NaN, +Inf
     and -Inf in one tensor's gradient (the codes and scales of a non-finite
     gradient are defined; the step of that tensor is outside the contract,
     but both paths run the same arithmetic on it)."""
     w = W.make(wl)
-    ref = GpuState(w, "cuda")
-    fus = GpuState(w, "cuda", fused=True)
+    if adam:
+        w.weight_decay = 0.1
+    ref = GpuState(w, "cuda", adam=adam)
+    fus = GpuState(w, "cuda", adam=adam, fused=True)
     big = max(range(w.n), key=lambda t: w.numel[t])
     for s in range(1, 5):
         for gs in (ref, fus):
@@ -73,8 +89,8 @@ def test_fused_equals_quantize_then_step_byte_for_byte(wl):
         torch.cuda.synchronize()
         a, b = _snapshot(ref, w.level), _snapshot(fus, w.level)
         for i, (x, y) in enumerate(zip(a, b)):
-            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (wl, s, i)
-    log("%s: fused and two-call paths identical over 4 steps" % wl)
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (wl, adam, s, i)
+    log("%s adam=%s: fused and two-call paths identical over 4 steps" % (wl, adam))
 
 
 def test_quantize_pass1_probe_touches_only_the_gradient_codes():

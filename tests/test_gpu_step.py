@@ -263,25 +263,38 @@ def test_rmw_probe_leaves_every_stream_unchanged():
     assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(after, before))
 
 
-@pytest.mark.parametrize("level,adam,wl", [("O2", False, "tiny_llama"), ("O3", True, "tiny_llama_o3"),
-                                           ("O2", False, "tiny_stress")])
-def test_graph_captured_step_replays_later_steps_bit_exact(level, adam, wl):
-    """amax + quantize + the device-constants step captured once in a HIP
-    graph (torch.cuda.graph) and replayed for steps 2..6, with the step's
-    constants rewritten in device memory and new gradients written between
-    replays (eager work and a synchronization in between every time). After
-    every replay the whole state equals the eager by-value entry points' bit
-    for bit."""
+@pytest.mark.parametrize("level,adam,wl,fused", [("O2", False, "tiny_llama", False),
+                                                 ("O3", True, "tiny_llama_o3", False),
+                                                 ("O2", False, "tiny_stress", False),
+                                                 ("O2", True, "tiny_stress", True),
+                                                 ("O3", False, "tiny_llama_o3", True)])
+def test_graph_captured_step_replays_later_steps_bit_exact(level, adam, wl, fused):
+    """amax + quantize + the device-constants step (or amax + the quantizing
+    device-constants step, fused=True) captured once in a HIP graph
+    (torch.cuda.graph) and replayed for steps 2..6, with the step's constants
+    rewritten in device memory and new gradients written between replays
+    (eager work and a synchronization in between every time). After every
+    replay the whole state equals the eager by-value unfused entry points'
+    bit for bit."""
     w = W.make(wl)
     if adam:
         w.weight_decay = 0.1
-    log("graph replay %s %s adam=%s" % (wl, level, adam))
+    log("graph replay %s %s adam=%s fused=%s" % (wl, level, adam, fused))
     ref = GpuState(w, "cuda", adam=adam)
     gr = GpuState(w, "cuda", adam=adam)
     consts = torch.empty(9, dtype=torch.float32, device="cuda")
 
     def graph_step():
         M.amax(gr.tl_g32, gr.grad_meta)
+        if fused and level == "O3":
+            M.quantize_adamw_o3_step_devconst(gr.tl_g32, w.grad_fmt, gr.grad_meta, gr.tl_gq, gr.tl_m,
+                                              gr.exp_avg_meta, gr.tl_v, gr.tl_w, gr.tl_w8, gr.weight_fp8_meta,
+                                              consts, adam=adam)
+            return
+        if fused:
+            M.quantize_adamw_o2_step_devconst(gr.tl_g32, w.grad_fmt, gr.grad_meta, gr.tl_gq, gr.tl_m,
+                                              gr.exp_avg_meta, gr.tl_v, gr.tl_w, consts, adam=adam)
+            return
         M.quantize_fp8(gr.tl_g32, w.grad_fmt, gr.grad_meta, gr.tl_gq)
         if level == "O3":
             M.adamw_o3_step_devconst(gr.tl_gq, w.grad_fmt, gr.grad_meta, gr.tl_m, gr.exp_avg_meta,
