@@ -216,6 +216,19 @@ def _role_ok(t: torch.Tensor, kind: str) -> bool:
     raise ValueError(kind)
 
 
+_SIZES = {}  # sizes tuple -> the one instance that equal TensorLists share
+
+
+def _shared_sizes(sizes) -> tuple:
+    t = tuple(sizes)
+    u = _SIZES.get(t)
+    if u is None:
+        if len(_SIZES) >= 256:
+            _SIZES.clear()
+        _SIZES[t] = u = t
+    return u
+
+
 class TensorList:
     """Pointer array and sizes of a list of device tensors, built once.
 
@@ -248,10 +261,12 @@ class TensorList:
             numel[i] = t.numel()
         self.ptrs = ptrs
         self.numel = numel
-        self.sizes = [t.numel() for t in self.tensors]
+        self.sizes = _shared_sizes(t.numel() for t in self.tensors)
 
     def matches(self, other: "TensorList", name: str) -> None:
-        if other.n != self.n or other.sizes != self.sizes:
+        # lists of equal sizes built in this process share one sizes tuple,
+        # so the usual check is an identity test, not n comparisons
+        if other.n != self.n or (other.sizes is not self.sizes and other.sizes != self.sizes):
             raise ValueError("%s does not match the tensor sizes of the list" % name)
         if other.n and other.device != self.device:
             raise ValueError("%s is on another device" % name)

@@ -37,7 +37,19 @@ msamp_status fail_hip(hipError_t e, const char* what) {
   return fail(MSAMP_E_HIP, msg);
 }
 
+#define MSAMP_TRY(expr)                 \
+  do {                                  \
+    msamp_status st__ = (expr);         \
+    if (st__ != MSAMP_OK) return st__;  \
+  } while (0)
+
 // ------------------------------------------------------------ profiler ---
+
+// Events created when timing is switched on (two per timed launch).
+constexpr size_t kProfilerReserve = 4096;
+// Timing events need no system-scope fence (nothing on the host reads the
+// memory the kernels write through them); without it a record costs less.
+constexpr unsigned kProfilerEventFlags = hipEventDisableSystemFence;
 
 struct Profiler {
   std::mutex mu;
@@ -57,7 +69,7 @@ struct Profiler {
       return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, kProfilerEventFlags) != hipSuccess) return nullptr;
     return e;
   }
   void recycle_all() {
@@ -68,9 +80,6 @@ struct Profiler {
     recs.clear();
   }
 };
-
-// Events created when timing is switched on (two per timed launch).
-constexpr size_t kProfilerReserve = 4096;
 
 Profiler& profiler() {
   static Profiler* p = new Profiler();  // never destroyed: events may outlive static teardown
@@ -140,6 +149,24 @@ struct PlanCache {
   size_t count = 0;
   size_t bytes = 0;
   uint64_t tick = 0;
+  // The plans each kind used last, most recent first: an optimizer passes
+  // the same few lists every step (two gradient buffers, say), so a call
+  // first compares its arrays with these in place.
+  static constexpr int kRecent = 4;
+  Plan* recent[16][kRecent] = {};
+
+  void forget(const Plan* p) {
+    for (auto& row : recent)
+      for (Plan*& r : row)
+        if (r == p) r = nullptr;
+  }
+  void touch(uint64_t kind, Plan* p) {
+    Plan** row = recent[kind];
+    int i = 0;
+    while (i < kRecent - 1 && row[i] != p) ++i;
+    for (; i > 0; --i) row[i] = row[i - 1];
+    row[0] = p;
+  }
 };
 
 PlanCache& cache() {
@@ -185,6 +212,7 @@ void evict_locked(PlanCache& c) {
     (void)hipDeviceSynchronize();
     c.bytes -= vec[best_idx]->bytes;
     c.count -= 1;
+    c.forget(vec[best_idx].get());
     vec.erase(vec.begin() + (ptrdiff_t)best_idx);
     if (vec.empty()) c.map.erase(best_hash);
     if (cur >= 0) (void)hipSetDevice(cur);
@@ -199,17 +227,80 @@ int64_t list_chunk_elems(int32_t n, const int64_t* numel) {
   return chunk_tiles_for(tiles) * kTile;
 }
 
+// True if 'p' was built for exactly these arrays: the same kind, tensor
+// count, sizes and role pointers (compared in place, without a key).
+bool same_list(const Plan* p, uint64_t kind, int32_t n, const int64_t* numel,
+               const void* const* const* ptrs, int nroles) {
+  static_assert(sizeof(void*) == sizeof(uint64_t) && sizeof(int64_t) == sizeof(uint64_t), "64-bit words");
+  const std::vector<uint64_t>& k = p->key;
+  const size_t nn = (size_t)n;
+  if (k.size() != 3 + nn * (1 + (size_t)nroles) || k[0] != kind || k[2] != (uint64_t)n) return false;
+  if (std::memcmp(&k[3], numel, nn * sizeof(uint64_t)) != 0) return false;
+  for (int r = 0; r < nroles; ++r) {
+    const uint64_t* seg = &k[3 + nn * (1 + (size_t)r)];
+    if (ptrs[r] != nullptr) {
+      if (std::memcmp(seg, ptrs[r], nn * sizeof(uint64_t)) != 0) return false;
+    } else {
+      for (size_t t = 0; t < nn; ++t)
+        if (seg[t] != 0) return false;
+    }
+  }
+  return true;
+}
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return capture != hipStreamCaptureStatusNone;
+}
+
+msamp_status check_list(int32_t n, const int64_t* numel, const void* const* ptrs, const char* role);
+msamp_status check_sizes(int32_t n, const int64_t* numel);
+
 // Returns the plan of a tensor list, building and uploading it (on 'stream')
 // the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n, or
-// null for a role the operation does not have): roles 0..4 fill p0..p4 of
-// the descriptors and role 5 fills aux;
+// null for a role the operation does not have, whose name is then null too):
+// roles 0..4 fill p0..p4 of the descriptors and role 5 fills aux;
 // 'min_one_chunk' gives every tensor at least one (possibly empty) chunk.
+// The per-tensor checks (sizes >= 0; pointers non-null where numel > 0 and
+// 16-byte aligned) run here, before any device call, for a list other than
+// those this kind used last: a list equal to a cached plan's passed them
+// when that plan was built.
 // On success '*lease' holds the cache lock: the caller keeps it until its
 // launches are enqueued, so that no other thread can evict (and free) the
 // plan in between.
 msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
-                      const void* const* const* ptrs, int nroles, bool min_one_chunk,
-                      hipStream_t stream, Plan** out, std::unique_lock<std::mutex>* lease) {
+                      const void* const* const* ptrs, const char* const* names, int nroles,
+                      bool min_one_chunk, hipStream_t stream, Plan** out,
+                      std::unique_lock<std::mutex>* lease) {
+  PlanCache& c = cache();
+  bool arrays_present = true;
+  for (int r = 0; r < nroles; ++r)
+    if (names[r] != nullptr && ptrs[r] == nullptr) arrays_present = false;
+  if (arrays_present) {
+    std::unique_lock<std::mutex> lk(c.mu);
+    for (int i = 0; i < PlanCache::kRecent; ++i) {
+      Plan* r = c.recent[kind][i];
+      if (r == nullptr || !same_list(r, kind, n, numel, ptrs, nroles)) continue;
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+      if ((uint64_t)dev != r->key[1]) continue;
+      if (stream_capturing(stream)) r->pinned = true;
+      r->last_use = ++c.tick;
+      c.touch(kind, r);
+      *out = r;
+      *lease = std::move(lk);
+      return MSAMP_OK;
+    }
+  }
+  MSAMP_TRY(check_sizes(n, numel));
+  for (int r = 0; r < nroles; ++r)
+    if (names[r] != nullptr) MSAMP_TRY(check_list(n, numel, ptrs[r], names[r]));
+
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -225,14 +316,8 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   const uint64_t h = hash_words(key);
 
   // A launch being captured into a graph keeps the plan's addresses: pin it.
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
-    (void)hipGetLastError();
-    capture = hipStreamCaptureStatusNone;
-  }
-  const bool capturing = capture != hipStreamCaptureStatusNone;
+  const bool capturing = stream_capturing(stream);
 
-  PlanCache& c = cache();
   std::unique_lock<std::mutex> lk(c.mu);
   auto it = c.map.find(h);
   if (it != c.map.end()) {
@@ -240,6 +325,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
       if (p->key == key) {
         p->last_use = ++c.tick;
         if (capturing) p->pinned = true;
+        c.touch(kind, p.get());
         *out = p.get();
         *lease = std::move(lk);
         return MSAMP_OK;
@@ -318,6 +404,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
 
   plan->last_use = ++c.tick;
   plan->pinned = capturing;
+  c.touch(kind, plan.get());
   *out = plan.get();
   c.bytes += plan->bytes;
   c.count += 1;
@@ -347,12 +434,23 @@ msamp_status check_list(int32_t n, const int64_t* numel, const void* const* ptrs
   return MSAMP_OK;
 }
 
-msamp_status check_common(int32_t n, const int64_t* numel) {
+// The tensor count and the sizes array (the sizes themselves are checked by
+// check_sizes, which get_plan runs for a list it has not just seen).
+msamp_status check_count(int32_t n, const int64_t* numel) {
   if (n < 0) return fail(MSAMP_E_INVALID_ARG, "n < 0");
   if (n > 0 && numel == nullptr) return fail(MSAMP_E_INVALID_ARG, "numel array is NULL");
+  return MSAMP_OK;
+}
+
+msamp_status check_sizes(int32_t n, const int64_t* numel) {
   for (int32_t t = 0; t < n; ++t)
     if (numel[t] < 0) return fail(MSAMP_E_INVALID_ARG, "numel[" + std::to_string(t) + "] < 0");
   return MSAMP_OK;
+}
+
+msamp_status check_common(int32_t n, const int64_t* numel) {
+  MSAMP_TRY(check_count(n, numel));
+  return check_sizes(n, numel);
 }
 
 msamp_status check_fmt(int fmt) {
@@ -402,12 +500,6 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
   return k;
 }
 
-#define MSAMP_TRY(expr)                 \
-  do {                                  \
-    msamp_status st__ = (expr);         \
-    if (st__ != MSAMP_OK) return st__;  \
-  } while (0)
-
 #define MSAMP_LAUNCH(kind, stream, call)                                   \
   do {                                                                     \
     hipError_t e__ = timed((kind), (stream), [&]() { return (call); });   \
@@ -454,6 +546,16 @@ msamp_status check_step_lists(bool o3, int32_t n, const int64_t* numel, const ui
   return MSAMP_OK;
 }
 
+// The meta arrays of an O2 (o3 = false) or O3 step (get_plan checks the
+// tensor lists).
+msamp_status check_step_meta(bool o3, int32_t n, const msamp_meta* grad_meta, const msamp_meta* exp_avg_meta,
+                             const msamp_meta* weight_fp8_meta) {
+  MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
+  MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
+  if (o3) MSAMP_TRY(check_meta(n, weight_fp8_meta, "weight_fp8_meta"));
+  return MSAMP_OK;
+}
+
 // The cached tables of a step's tensor lists (the same plan for every
 // entry point that takes these lists).
 msamp_status step_plan(bool o3, int32_t n, const int64_t* numel, const uint8_t* const* grad,
@@ -463,7 +565,8 @@ msamp_status step_plan(bool o3, int32_t n, const int64_t* numel, const uint8_t* 
   const void* const* roles[5] = {(const void* const*)grad, (const void* const*)exp_avg,
                                  (const void* const*)exp_avg_sq, (const void* const*)weight,
                                  (const void* const*)weight_fp8};
-  return get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, o3 ? 5 : 4, true, s, p, lease);
+  const char* names[5] = {"grad", "exp_avg", "exp_avg_sq", o3 ? "master" : "weight", "weight_fp8"};
+  return get_plan(o3 ? kPlanO3 : kPlanO2, n, numel, roles, names, o3 ? 5 : 4, true, s, p, lease);
 }
 
 msamp_status check_amax_array(int32_t n, const float* a, const char* role) {
@@ -479,7 +582,7 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
                        msamp_meta* weight_fp8_meta, const msamp_adamw_hparams* hp, int64_t step,
                        void* stream_ptr, const StepConsts* kdev = nullptr) {
   g_last_error.clear();
-  MSAMP_TRY(check_common(n, numel));
+  MSAMP_TRY(check_count(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
   if (kdev == nullptr) {
@@ -487,8 +590,7 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   } else if (((uintptr_t)kdev & 3u) != 0) {
     return fail(MSAMP_E_MISALIGNED, "consts is not 4-byte aligned");
   }
-  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
-                             weight, weight_fp8, weight_fp8_meta));
+  MSAMP_TRY(check_step_meta(o3, n, grad_meta, exp_avg_meta, weight_fp8_meta));
   hipStream_t s = (hipStream_t)stream_ptr;
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
@@ -522,7 +624,7 @@ msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t*
                                 const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr,
                                 const StepConsts* kdev = nullptr) {
   g_last_error.clear();
-  MSAMP_TRY(check_common(n, numel));
+  MSAMP_TRY(check_count(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
   if (kdev == nullptr) {
@@ -530,17 +632,19 @@ msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t*
   } else if (((uintptr_t)kdev & 3u) != 0) {
     return fail(MSAMP_E_MISALIGNED, "consts is not 4-byte aligned");
   }
-  MSAMP_TRY(check_list(n, numel, (const void* const*)grad_f32, "grad_f32"));
-  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq, weight,
-                             weight_fp8, weight_fp8_meta));
+  MSAMP_TRY(check_step_meta(o3, n, grad_meta, exp_avg_meta, weight_fp8_meta));
   hipStream_t s = (hipStream_t)stream_ptr;
   const void* const* roles[6] = {(const void* const*)grad,       (const void* const*)exp_avg,
                                  (const void* const*)exp_avg_sq, (const void* const*)weight,
                                  (const void* const*)weight_fp8, (const void* const*)grad_f32};
-  if (!o3) roles[4] = nullptr;
+  const char* names[6] = {"grad", "exp_avg", "exp_avg_sq", o3 ? "master" : "weight", "weight_fp8", "grad_f32"};
+  if (!o3) {
+    roles[4] = nullptr;
+    names[4] = nullptr;
+  }
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, 6, true, s, &p, &lease));
+  MSAMP_TRY(get_plan(o3 ? kPlanQuantizeO3 : kPlanQuantizeO2, n, numel, roles, names, 6, true, s, &p, &lease));
   const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
   MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE_PASS1, s,
                launch_quantize_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
@@ -567,14 +671,10 @@ msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* 
                                 msamp_meta* exp_avg_sq_meta, uint16_t* const* weight,
                                 const msamp_adamw_hparams* hp, int64_t step, void* stream_ptr) {
   g_last_error.clear();
-  MSAMP_TRY(check_common(n, numel));
+  MSAMP_TRY(check_count(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
   MSAMP_TRY(check_hparams(hp, step));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
   MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
   MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
   MSAMP_TRY(check_meta(n, exp_avg_sq_meta, "exp_avg_sq_meta"));
@@ -583,7 +683,8 @@ msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* 
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
+  const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_scaled_v_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -604,14 +705,10 @@ msamp_status step_delayed_impl(int32_t n, const int64_t* numel, const uint8_t* c
                                uint16_t* const* weight, const msamp_adamw_hparams* hp,
                                int64_t step, void* stream_ptr) {
   g_last_error.clear();
-  MSAMP_TRY(check_common(n, numel));
+  MSAMP_TRY(check_count(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
   MSAMP_TRY(check_hparams(hp, step));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
-  MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
   MSAMP_TRY(check_meta(n, grad_meta, "grad_meta"));
   MSAMP_TRY(check_meta(n, exp_avg_meta, "exp_avg_meta"));
   hipStream_t s = (hipStream_t)stream_ptr;
@@ -619,7 +716,8 @@ msamp_status step_delayed_impl(int32_t n, const int64_t* numel, const uint8_t* c
                                  (const void* const*)exp_avg_sq, (const void* const*)weight};
   Plan* p = nullptr;
   std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
+  const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
+  MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
   MSAMP_LAUNCH(MSAMP_KERNEL_O2_DELAYED, s,
                launch_step_delayed(grad_fmt, false, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -653,12 +751,11 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
                         const msamp_adamw_hparams* hp, int64_t step, float* amax_out,
                         const float* amax_in, void* stream_ptr) {
   g_last_error.clear();
-  MSAMP_TRY(check_common(n, numel));
+  MSAMP_TRY(check_count(n, numel));
   if (n == 0) return MSAMP_OK;
   MSAMP_TRY(check_fmt(grad_fmt));
   if (phase != 3) MSAMP_TRY(check_hparams(hp, step));
-  MSAMP_TRY(check_step_lists(o3, n, numel, grad, grad_meta, exp_avg, exp_avg_meta, exp_avg_sq,
-                             weight, weight_fp8, weight_fp8_meta));
+  MSAMP_TRY(check_step_meta(o3, n, grad_meta, exp_avg_meta, weight_fp8_meta));
   if (phase == 1 || (phase == 2 && o3)) MSAMP_TRY(check_amax_array(n, amax_out, "amax output"));
   if (phase >= 2) MSAMP_TRY(check_amax_array(n, amax_in, "amax input"));
   hipStream_t s = (hipStream_t)stream_ptr;
@@ -882,15 +979,15 @@ msamp_status msamp_amax(int32_t n, const float* const* x, const int64_t* numel, 
                         void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
-    MSAMP_TRY(check_common(n, numel));
+    MSAMP_TRY(check_count(n, numel));
     if (n == 0) return MSAMP_OK;
-    MSAMP_TRY(check_list(n, numel, (const void* const*)x, "x"));
     MSAMP_TRY(check_meta(n, meta, "meta"));
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[1] = {(const void* const*)x};
+    const char* names[1] = {"x"};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, 1, true, s, &p, &lease));
+    MSAMP_TRY(get_plan(kPlanAmax, n, numel, roles, names, 1, true, s, &p, &lease));
     MetaFold fold;  // small lists: the completing workgroup writes meta[t].amax
     if (p->nchunks <= kFoldMaxChunks) {
       fold.done = p->done;
@@ -909,18 +1006,17 @@ static msamp_status quantize_impl(int32_t n, const float* const* x, const int64_
                                   uint8_t* const* q, void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
-    MSAMP_TRY(check_common(n, numel));
+    MSAMP_TRY(check_count(n, numel));
     if (world < 1) return fail(MSAMP_E_INVALID_ARG, "world_size must be >= 1");
     if (n == 0) return MSAMP_OK;
     MSAMP_TRY(check_fmt((int)fmt));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)x, "x"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)q, "q"));
     MSAMP_TRY(check_meta(n, meta, "meta"));
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[2] = {(const void* const*)x, (const void* const*)q};
+    const char* names[2] = {"x", "q"};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-    MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, 2, true, s, &p, &lease));
+    MSAMP_TRY(get_plan(kPlanQuantize, n, numel, roles, names, 2, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE, s,
                  launch_quantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, world, s));
     return MSAMP_OK;
@@ -944,17 +1040,16 @@ msamp_status msamp_dequantize_fp8(int32_t n, const uint8_t* const* q, const int6
                                   float* const* out, void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
-    MSAMP_TRY(check_common(n, numel));
+    MSAMP_TRY(check_count(n, numel));
     if (n == 0) return MSAMP_OK;
     MSAMP_TRY(check_fmt((int)fmt));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)q, "q"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)out, "out"));
     MSAMP_TRY(check_meta(n, meta, "meta"));
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[2] = {(const void* const*)q, (const void* const*)out};
+    const char* names[2] = {"q", "out"};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launches are enqueued
-    MSAMP_TRY(get_plan(kPlanDequantize, n, numel, roles, 2, false, s, &p, &lease));
+    MSAMP_TRY(get_plan(kPlanDequantize, n, numel, roles, names, 2, false, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_DEQUANTIZE, s,
                  launch_dequantize((int)fmt, p->desc, p->chunks, p->nchunks, meta, s));
     return MSAMP_OK;
@@ -1251,6 +1346,7 @@ msamp_status msamp_release_cache(void) {
         if (!vec[i]->pinned) {
           c.bytes -= vec[i]->bytes;
           c.count -= 1;
+          c.forget(vec[i].get());
           vec.erase(vec.begin() + (ptrdiff_t)i);
         }
       it = vec.empty() ? c.map.erase(it) : std::next(it);
@@ -1293,20 +1389,16 @@ msamp_status msamp_quantize_pass1_probe(int32_t n, const int64_t* numel, const f
                                         uint16_t* const* exp_avg_sq, uint16_t* const* weight, void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
-    MSAMP_TRY(check_common(n, numel));
+    MSAMP_TRY(check_count(n, numel));
     if (n == 0) return MSAMP_OK;
-    MSAMP_TRY(check_list(n, numel, (const void* const*)grad_f32, "grad_f32"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[6] = {(const void* const*)grad,       (const void* const*)exp_avg,
                                    (const void* const*)exp_avg_sq, (const void* const*)weight,
                                    nullptr,                        (const void* const*)grad_f32};
+    const char* names[6] = {"grad", "exp_avg", "exp_avg_sq", "weight", nullptr, "grad_f32"};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;
-    MSAMP_TRY(get_plan(kPlanQuantizeO2, n, numel, roles, 6, true, s, &p, &lease));
+    MSAMP_TRY(get_plan(kPlanQuantizeO2, n, numel, roles, names, 6, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_QP1_PROBE, s, launch_qp1_probe(p->desc, p->chunks, p->nchunks, s));
     return MSAMP_OK;
   });
@@ -1343,18 +1435,15 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
                              uint16_t* const* weight, void* stream) {
   return guarded([&]() -> msamp_status {
     g_last_error.clear();
-    MSAMP_TRY(check_common(n, numel));
+    MSAMP_TRY(check_count(n, numel));
     if (n == 0) return MSAMP_OK;
-    MSAMP_TRY(check_list(n, numel, (const void* const*)grad, "grad"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg, "exp_avg"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)exp_avg_sq, "exp_avg_sq"));
-    MSAMP_TRY(check_list(n, numel, (const void* const*)weight, "weight"));
     hipStream_t s = (hipStream_t)stream;
     const void* const* roles[4] = {(const void* const*)grad, (const void* const*)exp_avg,
                                    (const void* const*)exp_avg_sq, (const void* const*)weight};
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;  // held until the launch is enqueued
-    MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, 4, true, s, &p, &lease));
+    const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
+    MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s));
     return MSAMP_OK;
   });
@@ -1388,7 +1477,7 @@ msamp_status msamp_profile_enable(int on) {
       // create the events up front, so that the timed work does not
       for (size_t i = p.pool.size(); i < kProfilerReserve; ++i) {
         hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) break;
+        if (hipEventCreateWithFlags(&e, kProfilerEventFlags) != hipSuccess) break;
         p.pool.push_back(e);
       }
     }
