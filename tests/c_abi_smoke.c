@@ -62,6 +62,21 @@ int main(void) {
                                       NULL) == MSAMP_E_INVALID_ARG, 16);
   EXPECT(strstr(msamp_last_error(), "weight_fp8[0]") != NULL, 17);
 
+  /* the Adam and device-constant forms check the same lists, and the
+   * device-constant forms refuse a NULL or misaligned constants record */
+  xf[0] = (const float*)(uintptr_t)0x700008;
+  EXPECT(msamp_quantize_adam_o2_step(1, numel, xf, MSAMP_FP8_E4M3, meta, gq, m, meta, v, w, &hp, 1, NULL) ==
+             MSAMP_E_MISALIGNED, 26);
+  xf[0] = (const float*)(uintptr_t)0x700000;
+  EXPECT(msamp_quantize_adam_o3_step(1, numel, xf, MSAMP_FP8_E5M2, meta, gq, m, meta, v, w, w8, meta, &hp, 1,
+                                     NULL) == MSAMP_E_INVALID_ARG, 27);
+  EXPECT(msamp_quantize_adamw_o2_step_devconst(1, numel, xf, MSAMP_FP8_E4M3, meta, gq, m, meta, v, w, NULL, 0,
+                                               NULL) == MSAMP_E_INVALID_ARG, 28);
+  EXPECT(strstr(msamp_last_error(), "consts") != NULL, 29);
+  const msamp_step_constants* kbad = (const msamp_step_constants*)(uintptr_t)0xA00002;
+  EXPECT(msamp_quantize_adamw_o3_step_devconst(1, numel, xf, MSAMP_FP8_E4M3, meta, gq, m, meta, v, w, w8, meta,
+                                               kbad, 1, NULL) == MSAMP_E_MISALIGNED, 30);
+
   /* measurement streams: size, alignment and overlap checks */
   void* src = (void*)(uintptr_t)0x800000;
   void* dst = (void*)(uintptr_t)0x800100;
