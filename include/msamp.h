@@ -83,7 +83,11 @@
  *     error nothing is enqueued and a status other than MSAMP_OK is returned,
  *     with a description from msamp_last_error() (per thread). No C++
  *     exception crosses this interface. Faults inside kernels surface at the
- *     caller's next synchronization.
+ *     caller's next synchronization. A call whose size and pointer arrays are
+ *     byte-equal to those of one of the last few lists of the same kind of
+ *     call reuses that list's tables without re-checking each tensor (those
+ *     arrays passed the checks when the tables were built); this changes the
+ *     cost of a call, never its outcome.
  *   - Different roles must not alias (e.g. exp_avg and weight); this is not
  *     checked.
  */
