@@ -75,8 +75,12 @@ def parse():
                         "(per-tensor-scaled FP16 second moment)")
     p.add_argument("--separate-quantize", action="store_true",
                    help="run the gradient quantize and the AdamW step as two calls (the default "
-                        "fuses the quantize into pass 1 of the step; Adam and the ablations always "
-                        "run the two calls)")
+                        "fuses the quantize into pass 1 of the AdamW or Adam step; the ablations "
+                        "always run the two calls)")
+    p.add_argument("--pad-gib", type=int, default=0, metavar="GIB",
+                   help="allocate (and keep) this many GiB of device memory before the workload's "
+                        "buffers, to move them to other physical memory (the update pass's rate "
+                        "depends on where its buffers land)")
     p.add_argument("--shard", type=int, default=1,
                    help="keep 1/N of every tensor (one data-parallel rank's share)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -634,6 +638,8 @@ def main() -> int:
         print("the %s ablation exists for the O2 layout only" % args.optimizer, file=sys.stderr)
         return 2
     fused = not (args.separate_quantize or delayed or scaled_v)
+    # held until the run ends, so the workload's buffers stay where it pushed them
+    pad = torch.empty(args.pad_gib << 30, dtype=torch.uint8, device=device) if args.pad_gib > 0 else None
     st = State(w, device, adam=adam, delayed=delayed, scaled_v=scaled_v, fused=fused)
     if args.graph:
         if delayed or scaled_v:
@@ -820,7 +826,7 @@ def main() -> int:
                                   ", HIP-graph replay" if args.graph else "",
                                   ", quantize fused with pass 1" if fused else ""),
                    "level": w.level, "optimizer": args.optimizer, "tensors": w.n, "params": P,
-                   "graph": bool(args.graph), "fused_quantize": fused},
+                   "graph": bool(args.graph), "fused_quantize": fused, "pad_gib": args.pad_gib},
         "hbm_gbps": round(gbps, 1),
         "pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_param": path_bytes,
