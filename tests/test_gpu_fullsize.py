@@ -52,11 +52,13 @@ def test_llama2_7b_o2_5_steps():
 
 
 def test_llama2_13b_o3_3_steps():
+    """The benchmark's O3 configuration: the gradient quantize fused with
+    pass 1 (msamp_quantize_adamw_o3_step)."""
     w = W.make("llama2_13b")
     verify = _first_last_layers(w, 39)
-    log("llama2_13b O3: %d tensors, %d params; verifying %d tensors (%d params)"
+    log("llama2_13b O3 fused: %d tensors, %d params; verifying %d tensors (%d params)"
         % (w.n, w.params, len(verify), sum(w.numel[t] for t in verify)))
-    stats, gs, _ = run_parity(w, 3, verify=verify, flat=True)
+    stats, gs, _ = run_parity(w, 3, verify=verify, flat=True, fused=True)
     _report("llama2_13b", stats)
     assert_bar(stats)
     _code_invariant(gs, w, verify)
@@ -69,6 +71,8 @@ def test_llama2_13b_o3_3_steps():
 
 
 def test_stress_e5m2_10_steps():
+    """The benchmark's configuration of the stress list: the gradient
+    quantize fused with pass 1."""
     w = W.make("stress")
     small = [t for t in range(w.n) if w.numel[t] <= 8192]
     big = [t for t in range(w.n) if w.numel[t] > 8192]
@@ -76,7 +80,7 @@ def test_stress_e5m2_10_steps():
     log("stress O2 E5M2: %d tensors, %d params; verifying the %d small tensors and 2 of the %d "
         "8192x8192 ones (%d params)" % (w.n, w.params, len(small), len(big),
                                         sum(w.numel[t] for t in verify)))
-    stats, gs, _ = run_parity(w, 10, verify=verify, flat=True)
+    stats, gs, _ = run_parity(w, 10, verify=verify, flat=True, fused=True)
     _report("stress", stats)
     assert_bar(stats)
     mm = gs.exp_avg_meta.cpu().numpy()
