@@ -15,6 +15,9 @@ Workloads (parameter lists of real model shapes; values are random):
   stress      20,000 tensors of log-uniform size in [64, 8192] plus 64 of
               8192x8192, O2, E5M2 grads from a Student-t (nu = 3) scaled by
               1e-3, with 1% of the tensors all-zero
+Test lists: tiny_llama / tiny_llama_o3 (reduced Llama shapes), tiny_stress
+(600 small + 2 larger tensors), tiny_small / tiny_small_o3 (1,122 tensors
+of at most 4,096 elements, with the edge sizes, between larger ones).
 Weights (or O3 master weights) are FP16 of N(0, 0.02). Optimizer states
 start at zero.
 """
@@ -122,6 +125,23 @@ def stress_shapes(n_small: int = 20000, n_big: int = 64, big: int = 8192 * 8192,
     return names, numel, frozenset(int(i) for i in zero)
 
 
+def small_shapes(seed: int = 2):
+    """Eight runs of small tensors (at most 4,096 elements: the edge sizes
+    around 1, 16, 1,024, 2,048 and 3,072 elements and 120 random ones from 0
+    to 4,096 each), separated by larger tensors, plus a lone small tensor
+    between two larger ones: 1,122 small tensors in all."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    edges = [0, 1, 3, 4, 5, 15, 16, 17, 1023, 1024, 1025, 2047, 2048, 2049, 3071, 3072, 3073, 4095, 4096, 7]
+    seps = [4097, 70001, 5000, 65536, 8191, 131075, 4100, 9999]
+    numel = []
+    for r in range(8):
+        numel += edges + [int(x) for x in rng.integers(0, 4097, 120)]
+        numel.append(seps[r])
+    numel += [12345, 2000, 77777, 300, 4097]
+    names = ["t%d" % i for i in range(len(numel))]
+    return names, numel
+
+
 # ---------------------------------------------------------------- workloads ---
 
 def make(name: str, shard: int = 1) -> Workload:
@@ -153,6 +173,10 @@ def make(name: str, shard: int = 1) -> Workload:
         f = np.exp(rng.uniform(math.log(0.1), math.log(10.0), len(ne)))
         level = "O3" if name.endswith("o3") else "O2"
         w = Workload(name, level, E4M3, 10, nm, ne, factor=f, seed_base=6)
+    elif name.startswith("tiny_small"):
+        nm, ne = small_shapes()
+        level = "O3" if name.endswith("o3") else "O2"
+        w = Workload(name, level, E5M2 if level == "O2" else E4M3, 3, nm, ne, seed_base=8)
     elif name == "tiny_stress":
         nm, ne, zero = stress_shapes(n_small=600, n_big=2, big=300_001, seed=1)
         w = Workload(name, "O2", E5M2, 10, nm, ne, grad_kind="student_t3", zero_tensors=zero,

@@ -267,7 +267,8 @@ def test_rmw_probe_leaves_every_stream_unchanged():
                                                  ("O3", True, "tiny_llama_o3", False),
                                                  ("O2", False, "tiny_stress", False),
                                                  ("O2", True, "tiny_stress", True),
-                                                 ("O3", False, "tiny_llama_o3", True)])
+                                                 ("O3", False, "tiny_llama_o3", True),
+                                                 ("O2", False, "tiny_small", True)])
 def test_graph_captured_step_replays_later_steps_bit_exact(level, adam, wl, fused):
     """amax + quantize + the device-constants step (or amax + the quantizing
     device-constants step, fused=True) captured once in a HIP graph
@@ -432,7 +433,8 @@ def _slice_bounds(numel, ranks):
 
 
 @pytest.mark.parametrize("level,adam,wl", [("O2", False, "tiny_llama"), ("O3", False, "tiny_llama_o3"),
-                                           ("O3", True, "tiny_llama_o3"), ("O2", True, "tiny_stress")])
+                                           ("O3", True, "tiny_llama_o3"), ("O2", True, "tiny_stress"),
+                                           ("O3", False, "tiny_small_o3")])
 def test_sharded_phases_equal_the_unsharded_step(level, adam, wl):
     """Three data-parallel ranks emulated on one GPU, each holding a slice of
     every tensor, run the split-phase step; the per-tensor amaxes are
