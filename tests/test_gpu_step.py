@@ -211,6 +211,47 @@ def test_deterministic_and_resume_bit_exact():
     assert all(torch.equal(x, y) for x, y in zip(snapshot(a), snapshot(b)))
 
 
+def test_nonfinite_gradient_step_is_skipped_and_training_resumes():
+    """The caller-side skip of a step on a non-finite gradient (what
+    GradScaler does; MS-AMP README, Usage): Inf and NaN planted in one tensor
+    make msamp_amax report a non-finite amax for that tensor only; the caller
+    reads the amax column, skips the quantize and the step, and the state is
+    untouched; the next step, with finite gradients and the same step count,
+    equals an uninterrupted run byte for byte."""
+    w = W.make("tiny_llama_o3")
+    ref = GpuState(w, "cuda")
+    sk = GpuState(w, "cuda")
+
+    def state(gs):
+        return [t.clone().view(torch.uint8) if t.dtype == torch.float16 else t.clone()
+                for t in gs.exp_avg + gs.exp_avg_sq + gs.weights + gs.weight_fp8 +
+                [gs.exp_avg_meta, gs.weight_fp8_meta]]
+
+    for gs in (ref, sk):
+        gs.fill_grads(1)
+        gs.step(1)
+    torch.cuda.synchronize()
+    before = state(sk)
+    bad = max(range(w.n), key=lambda t: w.numel[t])
+    sk.fill_grads(2)
+    sk.grad_f32[bad][3] = float("inf")
+    sk.grad_f32[bad][7] = float("nan")
+    M.amax(sk.tl_g32, sk.grad_meta)
+    amax = sk.grad_meta[:, 0]
+    finite = torch.isfinite(amax)
+    assert not bool(finite[bad]) and bool(finite[torch.arange(w.n, device="cuda") != bad].all())
+    skip = not bool(finite.all())
+    assert skip  # the caller enqueues neither the quantize nor the step
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(before, state(sk)))
+    # step 2 again with finite gradients
+    for gs in (ref, sk):
+        gs.fill_grads(2)
+        gs.step(2)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(state(ref), state(sk)))
+
+
 def test_o3_weight_copy_overwrites_every_element_and_max_code():
     w = W.Workload("cover", "O3", W.E4M3, 1, ["a", "b", "c"], [4097, 65537, 33], seed_base=12)
     gs = GpuState(w, "cuda")
