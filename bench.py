@@ -65,7 +65,8 @@ def kernel_source_hash() -> str:
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200,
+                   help="timed steps (default 200: about 5 s of GPU work on the 7B list)")
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama2_7b",
                    help="llama2_7b (default), llama2_13b, gpt2_small, single_1m, stress")
