@@ -165,3 +165,21 @@ def test_llama2_7b_fused_quantize_step_3_steps():
     _code_invariant(gs, w, verify)
     del gs
     torch.cuda.empty_cache()
+
+
+def test_llama2_7b_fused_adam_2_steps():
+    """Adam (coupled L2) through the fused quantize-step over the whole 7B
+    list (what bench.py --optimizer adam times), one tensor of every
+    distinct size checked against the oracle."""
+    w = W.make("llama2_7b")
+    w.weight_decay = 0.1
+    verify = [w.names.index(nm) for nm in ("embed_tokens", "layers.5.q_proj", "layers.5.gate_proj",
+                                            "layers.5.post_attention_layernorm")]
+    assert set(w.numel[t] for t in verify) == set(w.numel)
+    log("llama2_7b O2 fused Adam: verifying %d tensors (%d params)" % (len(verify), sum(w.numel[t] for t in verify)))
+    stats, gs, _ = run_parity(w, 2, verify=verify, flat=True, fused=True, adam=True)
+    _report("llama2_7b fused adam", stats)
+    assert_bar(stats)
+    _code_invariant(gs, w, verify)
+    del gs
+    torch.cuda.empty_cache()
