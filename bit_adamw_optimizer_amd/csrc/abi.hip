@@ -132,6 +132,7 @@ struct Plan {
   TensorDesc* desc = nullptr;
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
+  bool wide = false;  // chunks of kWideChunk for kWideBlock-thread step passes
   uint64_t last_use = 0;
   // Used by a launch captured into a graph: its memory stays until
   // msamp_unpin_captured_tables(), since a replay reads and writes it.
@@ -219,12 +220,18 @@ void evict_locked(PlanCache& c) {
   }
 }
 
-// Elements per chunk of a list: whole tiles, fewer per chunk for a small
-// list so that its launches still spread over every compute unit.
-int64_t list_chunk_elems(int32_t n, const int64_t* numel) {
+int64_t list_tiles(int32_t n, const int64_t* numel) {
   int64_t tiles = 0;
   for (int32_t t = 0; t < n; ++t) tiles += (numel[t] + kTile - 1) / kTile;
-  return chunk_tiles_for(tiles) * kTile;
+  return tiles;
+}
+
+// Elements per chunk of a list: whole tiles, fewer per chunk for a small
+// list so that its launches still spread over every compute unit.
+int64_t list_chunk_elems(int32_t n, const int64_t* numel) { return chunk_tiles_for(list_tiles(n, numel)) * kTile; }
+
+bool is_step_plan(uint64_t kind) {
+  return kind == kPlanO2 || kind == kPlanO3 || kind == kPlanQuantizeO2 || kind == kPlanQuantizeO3;
 }
 
 // True if 'p' was built for exactly these arrays: the same kind, tensor
@@ -332,8 +339,10 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
       }
   }
 
-  // Build the chunk map (chunks of list_chunk_elems elements).
-  const int64_t ce = list_chunk_elems(n, numel);
+  // Build the chunk map: chunks of list_chunk_elems elements, or of
+  // kWideChunk for the step passes of a large list (wide workgroups).
+  const bool wide = is_step_plan(kind) && list_tiles(n, numel) >= kWideMinTiles;
+  const int64_t ce = wide ? kWideChunk : list_chunk_elems(n, numel);
   std::vector<ChunkRef> chunks;
   int64_t total = 0;
   for (int32_t t = 0; t < n; ++t) {
@@ -398,6 +407,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   plan->desc = (TensorDesc*)(db + scratch_bytes);
   plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
   plan->nchunks = (int64_t)chunks.size();
+  plan->wide = wide;
 
   e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail_hip(e, "upload of the descriptor tables");
@@ -512,6 +522,8 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
 // finalize launch, which avoids one counter atomic per workgroup.
 constexpr int64_t kFoldMaxChunks = 8192;
 
+bool wide_launch(const Plan* p) { return p->wide; }
+
 // The meta writes of a step folded into its last pass (pass 2 for O2,
 // pass 3 for O3), or none for a large list.
 MetaFold step_fold(const Plan* p, bool o3, msamp_meta* exp_avg_meta, msamp_meta* weight_fp8_meta) {
@@ -599,14 +611,15 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
 
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, k, s, kdev));
+                                 exp_avg_meta, p->scratch_a, k, s, kdev, wide_launch(p)));
   const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev, o3 ? MetaFold{} : fold));
+                                 exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev, o3 ? MetaFold{} : fold,
+                                 wide_launch(p)));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p)));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
@@ -648,15 +661,15 @@ msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t*
   const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
   MSAMP_LAUNCH(MSAMP_KERNEL_QUANTIZE_PASS1, s,
                launch_quantize_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta, exp_avg_meta,
-                                     p->scratch_a, k, s, kdev));
+                                     p->scratch_a, k, s, kdev, wide_launch(p)));
   const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev,
-                                 o3 ? MetaFold{} : fold));
+                                 o3 ? MetaFold{} : fold, wide_launch(p)));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p)));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
@@ -766,7 +779,7 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
     const StepConsts k = make_consts(hp, step, coupled);
     MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
                  launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                   exp_avg_meta, p->scratch_a, k, s));
+                                   exp_avg_meta, p->scratch_a, k, s, nullptr, wide_launch(p)));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_a, amax_out, s));
   } else if (phase == 2) {
     const StepConsts k = make_consts(hp, step, coupled);
@@ -774,12 +787,14 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
     // unsigned integers the update pass reads
     MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                  launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
-                                   exp_avg_meta, (const uint32_t*)amax_in, p->scratch_b, k, s));
+                                   exp_avg_meta, (const uint32_t*)amax_in, p->scratch_b, k, s, nullptr,
+                                   MetaFold{}, wide_launch(p)));
     if (o3) MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_b, amax_out, s));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_meta_from_amax(n, amax_in, exp_avg_meta, 448.0f, s));
   } else {
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, (const uint32_t*)amax_in, s));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, (const uint32_t*)amax_in, s, MetaFold{},
+                                 wide_launch(p)));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_meta_from_amax(n, amax_in, weight_fp8_meta, 448.0f, s));
   }
@@ -1399,7 +1414,7 @@ msamp_status msamp_quantize_pass1_probe(int32_t n, const int64_t* numel, const f
     Plan* p = nullptr;
     std::unique_lock<std::mutex> lease;
     MSAMP_TRY(get_plan(kPlanQuantizeO2, n, numel, roles, names, 6, true, s, &p, &lease));
-    MSAMP_LAUNCH(MSAMP_KERNEL_QP1_PROBE, s, launch_qp1_probe(p->desc, p->chunks, p->nchunks, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_QP1_PROBE, s, launch_qp1_probe(p->desc, p->chunks, p->nchunks, s, wide_launch(p)));
     return MSAMP_OK;
   });
 }
@@ -1444,7 +1459,7 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
     std::unique_lock<std::mutex> lease;  // held until the launch is enqueued
     const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
     MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
-    MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s));
+    MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s, wide_launch(p)));
     return MSAMP_OK;
   });
 }

@@ -4,9 +4,10 @@
 // O3 and the optimization-level table).
 //
 // All kernels are multi-tensor-apply launches: workgroup b takes ChunkRef b
-// (tensor t, chunk j) and covers elements [j*kChunk, min(numel, (j+1)*kChunk))
-// of tensor t through the 64-byte TensorDesc of t, in tiles of 4096
-// elements (4 waves x 1024). Inside a wave's 1024 elements the lanes are laid
+// (tensor t, chunk j) and covers elements [j*c, min(numel, (j+1)*c)) of
+// tensor t (c: the list's chunk size, in its TensorDesc) in tiles of 16
+// elements per thread: 4,096 elements (4 waves x 1024), or 8,192 (8 waves)
+// for the step passes of a large list. Inside a wave's 1024 elements the lanes are laid
 // out so that every load and store instruction of the wave covers one
 // contiguous span of memory:
 //   FP8 / FP16 streams: lane l owns the 8-element groups at l*8 and
@@ -36,16 +37,16 @@ namespace {
 // partials before thread 0 has read them.
 // WAIT: thread 0 waits until its update has been performed (the folded
 // meta write of the same launch counts this workgroup only after that).
-template <bool WAIT = false>
+template <bool WAIT = false, int BS = kBlock>
 __device__ __forceinline__ void block_max_into(uint32_t v, uint32_t* dst) {
-  __shared__ uint32_t partial[kBlock / 64];
+  __shared__ uint32_t partial[BS / 64];
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = partial[0];
 #pragma unroll
-    for (int k = 1; k < kBlock / 64; ++k) m = umax(m, partial[k]);
+    for (int k = 1; k < BS / 64; ++k) m = umax(m, partial[k]);
     if (WAIT)
       atomic_max_if_larger_wait(m, dst);
     else
@@ -293,8 +294,8 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const TensorDesc* __restr
 // (COUPLED) also reads the weight for its L2 term. The step constants come
 // by value (kv), or from device memory when kdev is not null (so that a
 // captured launch can be replayed for later steps).
-template <int GF, bool COUPLED>
-__global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restrict__ desc,
+template <int GF, bool COUPLED, int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_step_pass1(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
                                                        const msamp_meta* __restrict__ mmeta,
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
   const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
   const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   uint32_t mx = 0u;
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
     if (!COUPLED && group16_base(tile) + 16 <= r.end) {
       // only FP8 streams: 16 consecutive codes per lane, one 16-byte
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass1(const TensorDesc* __restr
       }
     }
   }
-  block_max_into(mx, &amax_m[r.t]);
+  block_max_into<false, BS>(mx, &amax_m[r.t]);
 }
 
 // Gradient quantize fused with pass 1 (O2 and O3; AdamW, or Adam when
@@ -400,8 +401,8 @@ __device__ __forceinline__ uint32_t qp1_group(const StepConsts& k, const u32x4& 
   return mx;
 }
 
-template <int GF, bool COUPLED>
-__global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __restrict__ desc,
+template <int GF, bool COUPLED, int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_quantize_pass1(const TensorDesc* __restrict__ desc,
                                                            const ChunkRef* __restrict__ chunks,
                                                            msamp_meta* __restrict__ gmeta,
                                                            const msamp_meta* __restrict__ mmeta,
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __r
   const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   const u32x2 nowt = {0u, 0u};
   uint32_t mx = 0u;
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     if (group4_base(tile, 3) + 4 <= r.end) {
       u32x4 v[4];
       uint32_t mw[4];
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __r
       }
     }
   }
-  block_max_into(mx, &amax_m[r.t]);
+  block_max_into<false, BS>(mx, &amax_m[r.t]);
 }
 
 // Pass 2: recompute m1 exactly as in pass 1, then v1, w1; store m (E4M3 with
@@ -471,8 +472,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pass1(const TensorDesc* __r
 // DELAYED (an ablation of the two-pass scheme, O2 only): the codes are
 // encoded with the scale of the previous step's amax (mmeta.amax) and the
 // amax of the new m1 is reduced into amax_w for the next step.
-template <int GF, bool O3, bool COUPLED, bool DELAYED = false>
-__global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restrict__ desc,
+template <int GF, bool O3, bool COUPLED, bool DELAYED = false, int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_step_pass2(const TensorDesc* __restrict__ desc,
                                                        const ChunkRef* __restrict__ chunks,
                                                        const msamp_meta* __restrict__ gmeta,
                                                        const msamp_meta* __restrict__ mmeta,
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
   GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
   GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   uint32_t wmax = 0u;  // FP16 magnitude bits of the new weight (O3)
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
     if (e1 + 8 <= r.end) {
       const u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
@@ -558,21 +559,22 @@ __global__ __launch_bounds__(kBlock) void k_step_pass2(const TensorDesc* __restr
     // magnitude of the largest stored master value as binary32 bits; the
     // binary16 -> binary32 widening is exact and preserves the order
     const uint32_t bits = abs_bits(h_to_f((uint16_t)wmax));
-    block_max_into(bits, &amax_w[r.t]);
+    block_max_into<false, BS>(bits, &amax_w[r.t]);
   }
-  if (DELAYED) block_max_into(mmax, &amax_w[r.t]);
+  if (DELAYED) block_max_into<false, BS>(mmax, &amax_w[r.t]);
   if (!O3 && !DELAYED) fold_meta<false>(fold, desc, r.t);  // O3: the fold is in pass 3
 }
 
 // Pass 3 (O3): FP8 E4M3 copy of the stored master with its own scale.
-__global__ __launch_bounds__(kBlock) void k_o3_pass3(const TensorDesc* __restrict__ desc,
+template <int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_o3_pass3(const TensorDesc* __restrict__ desc,
                                                      const ChunkRef* __restrict__ chunks,
                                                      const uint32_t* __restrict__ amax_w, MetaFold fold) {
   const ChunkRange r = chunk_range(chunks, desc);
   const float s_w = scale_rule(__uint_as_float(amax_w[r.t]), kE4M3Max);
   const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   GLOBAL uint8_t* __restrict__ w8 = global_ptr<uint8_t>(desc[r.t].p4);
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
     if (e1 + 8 <= r.end) {
       float w[16];
@@ -795,14 +797,15 @@ __global__ __launch_bounds__(kBlock) void k_delayed_finalize(int32_t n, uint32_t
 // v, w and write m, v, w back unchanged (the empty asm keeps the compiler
 // from treating the stores of just-loaded values as removable). It measures
 // what the memory system gives this traffic on the very same buffers.
-__global__ __launch_bounds__(kBlock) void k_rmw_probe(const TensorDesc* __restrict__ desc,
+template <int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_rmw_probe(const TensorDesc* __restrict__ desc,
                                                       const ChunkRef* __restrict__ chunks) {
   const ChunkRange r = chunk_range(chunks, desc);
   const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
   GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
   GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
   GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     const int64_t e0 = group8_base(tile), e1 = e0 + 512;
     if (e1 + 8 <= r.end) {
       u32x2 G0 = load<u32x2>(gq + e0), G1 = load<u32x2>(gq + e1);
@@ -836,13 +839,14 @@ __global__ __launch_bounds__(kBlock) void k_rmw_probe(const TensorDesc* __restri
 // (measurement aid): the same lanes, tiles and launch; reads the binary32
 // gradient (aux) and the first-moment codes (p1) and writes an unspecified
 // mix of them to the gradient codes (p0), 6 bytes per element.
-__global__ __launch_bounds__(kBlock) void k_qp1_probe(const TensorDesc* __restrict__ desc,
+template <int BS = kBlock>
+__global__ __launch_bounds__(BS) void k_qp1_probe(const TensorDesc* __restrict__ desc,
                                                       const ChunkRef* __restrict__ chunks) {
   const ChunkRange r = chunk_range(chunks, desc);
   const GLOBAL float* __restrict__ x = global_ptr<float>(desc[r.t].aux);
   GLOBAL uint8_t* __restrict__ q = global_ptr<uint8_t>(const_cast<void*>(desc[r.t].p0));
   const GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
-  for (int64_t tile = r.begin; tile < r.end; tile += kTile) {
+  for (int64_t tile = r.begin; tile < r.end; tile += (int64_t)BS * 16) {
     if (group4_base(tile, 3) + 4 <= r.end) {
       u32x4 v[4];
       uint32_t mw[4];
@@ -987,67 +991,87 @@ hipError_t launch_dequantize(int fmt, const TensorDesc* desc, const ChunkRef* ch
   return hipGetLastError();
 }
 
-template <int GF, bool COUPLED>
+template <int GF, bool COUPLED, int BS>
 static void pass1_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
                          const StepConsts& k, const StepConsts* kdev) {
-  k_step_pass1<GF, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  k_step_pass1<GF, COUPLED, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+}
+
+template <int BS>
+static void pass1_dispatch(int gfmt, bool coupled, unsigned g, hipStream_t stream, const TensorDesc* desc,
+                           const ChunkRef* chunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
+                           uint32_t* amax_m, const StepConsts& k, const StepConsts* kdev) {
+  if (gfmt == kE4M3) {
+    if (coupled) pass1_launch<kE4M3, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else pass1_launch<kE4M3, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  } else {
+    if (coupled) pass1_launch<kE5M2, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else pass1_launch<kE5M2, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  }
+}
+
+template <int BS>
+static void qp1_dispatch(int gfmt, bool coupled, unsigned g, hipStream_t stream, const TensorDesc* desc,
+                         const ChunkRef* chunks, msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
+                         const StepConsts& k, const StepConsts* kdev) {
+  if (gfmt == kE4M3) {
+    if (coupled)
+      k_quantize_pass1<kE4M3, true, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else
+      k_quantize_pass1<kE4M3, false, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  } else {
+    if (coupled)
+      k_quantize_pass1<kE5M2, true, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+    else
+      k_quantize_pass1<kE5M2, false, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  }
 }
 
 hipError_t launch_quantize_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                                  int64_t nchunks, msamp_meta* gmeta, const msamp_meta* mmeta, uint32_t* amax_m,
-                                 const StepConsts& k, hipStream_t stream, const StepConsts* kdev) {
+                                 const StepConsts& k, hipStream_t stream, const StepConsts* kdev, bool wide) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
-  if (gfmt == kE4M3) {
-    if (coupled)
-      k_quantize_pass1<kE4M3, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-    else
-      k_quantize_pass1<kE4M3, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-  } else {
-    if (coupled)
-      k_quantize_pass1<kE5M2, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-    else
-      k_quantize_pass1<kE5M2, false><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-  }
+  if (wide)
+    qp1_dispatch<kWideBlock>(gfmt, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  else
+    qp1_dispatch<kBlock>(gfmt, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
   return hipGetLastError();
 }
 
 hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, const ChunkRef* chunks,
                              int64_t nchunks, const msamp_meta* gmeta, const msamp_meta* mmeta,
                              uint32_t* amax_m, const StepConsts& k, hipStream_t stream,
-                             const StepConsts* kdev) {
+                             const StepConsts* kdev, bool wide) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
-  if (gfmt == kE4M3) {
-    if (coupled) pass1_launch<kE4M3, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-    else pass1_launch<kE4M3, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-  } else {
-    if (coupled) pass1_launch<kE5M2, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-    else pass1_launch<kE5M2, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
-  }
+  if (wide)
+    pass1_dispatch<kWideBlock>(gfmt, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
+  else
+    pass1_dispatch<kBlock>(gfmt, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, k, kdev);
   return hipGetLastError();
 }
 
-template <int GF, bool O3, bool COUPLED>
+template <int GF, bool O3, bool COUPLED, int BS>
 static void pass2_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, const uint32_t* amax_m,
                          uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev, const MetaFold& fold) {
-  k_step_pass2<GF, O3, COUPLED><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k,
-                                                          kdev, fold);
+  k_step_pass2<GF, O3, COUPLED, false, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k,
+                                                                 kdev, fold);
 }
 
-template <int GF>
+template <int GF, int BS>
 static void pass2_dispatch(bool o3, bool coupled, unsigned g, hipStream_t stream,
                            const TensorDesc* desc, const ChunkRef* chunks, const msamp_meta* gmeta,
                            const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                            const StepConsts& k, const StepConsts* kdev, const MetaFold& f) {
   if (o3) {
-    if (coupled) pass2_launch<GF, true, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
-    else pass2_launch<GF, true, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    if (coupled) pass2_launch<GF, true, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    else pass2_launch<GF, true, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
   } else {
-    if (coupled) pass2_launch<GF, false, true>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
-    else pass2_launch<GF, false, false>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    if (coupled) pass2_launch<GF, false, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    else pass2_launch<GF, false, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
   }
 }
 
@@ -1055,13 +1079,20 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                              const StepConsts& k, hipStream_t stream, const StepConsts* kdev,
-                             const MetaFold& fold) {
+                             const MetaFold& fold, bool wide) {
   if (nchunks <= 0) return hipSuccess;
   const unsigned g = grid_of(nchunks);
-  if (gfmt == kE4M3)
-    pass2_dispatch<kE4M3>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
-  else
-    pass2_dispatch<kE5M2>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+  if (gfmt == kE4M3) {
+    if (wide)
+      pass2_dispatch<kE4M3, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+    else
+      pass2_dispatch<kE4M3, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+  } else {
+    if (wide)
+      pass2_dispatch<kE5M2, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+    else
+      pass2_dispatch<kE5M2, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+  }
   return hipGetLastError();
 }
 
@@ -1118,9 +1149,12 @@ hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* me
 }
 
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold) {
+                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold, bool wide) {
   if (nchunks <= 0) return hipSuccess;
-  k_o3_pass3<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, amax_w, fold);
+  if (wide)
+    k_o3_pass3<kWideBlock><<<grid_of(nchunks), kWideBlock, 0, stream>>>(desc, chunks, amax_w, fold);
+  else
+    k_o3_pass3<kBlock><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, amax_w, fold);
   return hipGetLastError();
 }
 
@@ -1165,16 +1199,23 @@ hipError_t launch_stream_probe(bool copy, const void* src, void* dst, int64_t by
   return hipGetLastError();
 }
 
-hipError_t launch_qp1_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks, hipStream_t stream) {
+hipError_t launch_qp1_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks, hipStream_t stream,
+                            bool wide) {
   if (nchunks <= 0) return hipSuccess;
-  k_qp1_probe<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
+  if (wide)
+    k_qp1_probe<kWideBlock><<<grid_of(nchunks), kWideBlock, 0, stream>>>(desc, chunks);
+  else
+    k_qp1_probe<kBlock><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
   return hipGetLastError();
 }
 
 hipError_t launch_rmw_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool wide) {
   if (nchunks <= 0) return hipSuccess;
-  k_rmw_probe<<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
+  if (wide)
+    k_rmw_probe<kWideBlock><<<grid_of(nchunks), kWideBlock, 0, stream>>>(desc, chunks);
+  else
+    k_rmw_probe<kBlock><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
   return hipGetLastError();
 }
 

@@ -29,6 +29,11 @@ def test_kernel_names_map_to_kinds_and_bytes():
         "k_o3_pass3" + args: ("o3_pass3", 3),
         "k_quantize_pass1<0, false>" + args: ("quantize_pass1", 6),
         "k_quantize_pass1<1, true>" + args: ("quantize_pass1", 8),
+        "k_quantize_pass1<0, false, 512>" + args: ("quantize_pass1", 6),
+        "k_step_pass2<0, false, false, false, 512>" + args: ("o2_pass2", 11),
+        "k_step_pass2<0, true, false, false, 512>" + args: ("o3_pass2", 11),
+        "k_o3_pass3<512>" + args: ("o3_pass3", 3),
+        "k_rmw_probe<512>" + args: ("rmw_probe", 11),
         "k_rmw_probe" + args: ("rmw_probe", 11),
         "k_scaled_v_pass1<0>" + args: ("step_pass1", 4),
         "k_scaled_v_pass2<0>" + args: ("o2_pass2", 11),
