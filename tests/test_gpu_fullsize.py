@@ -183,3 +183,88 @@ def test_llama2_7b_fused_adam_2_steps():
     _code_invariant(gs, w, verify)
     del gs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("level,gfmt", [("O2", "E4M3"), ("O3", "E5M2")])
+def test_wide_chunks_with_folded_meta_writes(level, gfmt):
+    """One tensor of exactly 2^30 elements: the smallest list whose step
+    passes run the wide launch (512-thread workgroups, 131,072-element
+    chunks) and the largest whose 8,192 chunks still fold the meta writes
+    into the last pass (no finalize launch). Two fused quantize-steps (the
+    benchmark's path) checked against the oracle on windows at the start,
+    the middle and the end, with the tensor's largest |gradient| (and, for
+    O3, largest |master weight|) planted inside them, so that the oracle run
+    on the windows sees the whole tensor's scales (the argument of the
+    2^32 + 4099 test above). Gradient magnitudes lie in [0.5, 1], with
+    alternating signs: (1 - beta2) g^2 then stays a normal binary16 number,
+    so no weight takes the large step a zero FP16 second moment gives, and
+    the planted master weight stays the largest."""
+    import bit_adamw_optimizer_amd as M
+    import oracle as O
+    from tests.parity import Stats, u32
+
+    dev = "cuda"
+    fmt = getattr(O, gfmt)
+    n = 1 << 30
+    g_plant, w_plant = (1 << 29) + 77, 1234
+    wins = [(0, 60_000), ((1 << 29) - 60_000, (1 << 29) + 60_000), (n - 60_000, n)]
+    assert all(b <= c for (_, b), (c, _) in zip(wins, wins[1:]))
+    assert wins[1][0] <= g_plant < wins[1][1] and wins[0][0] <= w_plant < wins[0][1]
+    idx = torch.cat([torch.arange(a, b, device=dev) for a, b in wins])
+    log("%s %s: one tensor of 2^30 elements; checking %d of them" % (level, gfmt, idx.numel()))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    w = (torch.randn(n, generator=gen, device=dev) * 0.02).to(torch.float16)
+    if level == "O3":
+        w[w_plant] = 1.0
+    m = torch.zeros(n, dtype=torch.uint8, device=dev)
+    v = torch.zeros(n, dtype=torch.float16, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    x = torch.empty(n, dtype=torch.float32, device=dev)
+    w8 = torch.zeros(n, dtype=torch.uint8, device=dev) if level == "O3" else None
+    gmeta, mmeta = M.new_meta(1, dev), M.new_meta(1, dev)
+    w8meta = M.new_meta(1, dev) if level == "O3" else None
+    hp = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    torch.cuda.synchronize()
+    ost = O.TensorState(w[idx].cpu().numpy().view(np.uint16), level)
+    stats = {k: Stats() for k in ("m", "v", "w", "w8")}
+    M.release_cache()
+    for s in (1, 2):
+        x.uniform_(0.5, 1.0, generator=gen)
+        x[::2].neg_()
+        x[g_plant] = 2.0
+        M.amax([x], gmeta)
+        torch.cuda.synchronize()
+        before = M.cache_stats()["bytes"]
+        M.profile_enable(True)
+        if level == "O2":
+            M.quantize_adamw_o2_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], step=s, **hp)
+        else:
+            M.quantize_adamw_o3_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], [w8], w8meta, step=s, **hp)
+        torch.cuda.synchronize()
+        launches = {k: M.profile_read(k)[0] for k in ("quantize_pass1", "o2_pass2", "o3_pass2", "o3_pass3",
+                                                      "finalize")}
+        M.profile_enable(False)
+        assert launches["finalize"] == 0, launches
+        assert launches["quantize_pass1"] == 1 and launches["o3_pass3"] == (1 if level == "O3" else 0), launches
+        if s == 1:
+            # the step's tables: 256 B of amax words, 256 B of descriptors and
+            # 8,192 chunk references of 8 B (16,384 for 65,536-element chunks)
+            assert M.cache_stats()["bytes"] - before == 256 + 256 + 8192 * 8
+        qg, gm = O.step_tensor(ost, x[idx].cpu().numpy(), fmt, s, **hp)
+        assert np.array_equal(u32(gmeta[0, :3].cpu().numpy()), u32(gm[:3])), (gmeta, gm)
+        assert np.array_equal(q[idx].cpu().numpy(), qg)
+        where = "step %d" % s
+        stats["m"].add(m[idx].cpu().numpy(), ost.m, "fp8", where)
+        stats["v"].add(v[idx].cpu().numpy().view(np.uint16), ost.v, "f16", where)
+        stats["w"].add(w[idx].cpu().numpy().view(np.uint16), ost.w, "f16", where)
+        assert np.array_equal(u32(mmeta[0, :3].cpu().numpy()), u32(ost.m_meta[:3]))
+        assert int(m[g_plant]) == 0x7E
+        if level == "O3":
+            stats["w8"].add(w8[idx].cpu().numpy(), ost.w8, "fp8", where)
+            assert np.array_equal(u32(w8meta[0, :3].cpu().numpy()), u32(ost.w8_meta[:3]))
+            assert int(w8[w_plant]) & 0x7F == 0x7E
+        _report("2^30 %s step %d" % (level, s), stats)
+    assert_bar(stats)
+    del x, q, m, v, w, w8
+    torch.cuda.empty_cache()
