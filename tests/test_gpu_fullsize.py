@@ -185,8 +185,9 @@ def test_llama2_7b_fused_adam_2_steps():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("level,gfmt", [("O2", "E4M3"), ("O3", "E5M2")])
-def test_wide_chunks_with_folded_meta_writes(level, gfmt):
+@pytest.mark.parametrize("level,gfmt,adam", [("O2", "E4M3", False), ("O3", "E5M2", False), ("O2", "E5M2", True),
+                                             ("O3", "E4M3", True), ("O3", "E5M2", True)])
+def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam):
     """One tensor of exactly 2^30 elements: the smallest list whose step
     passes run the wide launch (512-thread workgroups, 131,072-element
     chunks) and the largest whose 8,192 chunks still fold the meta writes
@@ -198,7 +199,8 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt):
     2^32 + 4099 test above). Gradient magnitudes lie in [0.5, 1], with
     alternating signs: (1 - beta2) g^2 then stays a normal binary16 number,
     so no weight takes the large step a zero FP16 second moment gives, and
-    the planted master weight stays the largest."""
+    the planted master weight stays the largest. Adam (coupled L2) adds
+    wd * w to each gradient, far below the planted one."""
     import bit_adamw_optimizer_amd as M
     import oracle as O
     from tests.parity import Stats, u32
@@ -211,7 +213,8 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt):
     assert all(b <= c for (_, b), (c, _) in zip(wins, wins[1:]))
     assert wins[1][0] <= g_plant < wins[1][1] and wins[0][0] <= w_plant < wins[0][1]
     idx = torch.cat([torch.arange(a, b, device=dev) for a, b in wins])
-    log("%s %s: one tensor of 2^30 elements; checking %d of them" % (level, gfmt, idx.numel()))
+    log("%s %s%s: one tensor of 2^30 elements; checking %d of them" % (level, gfmt, " Adam" if adam else "",
+                                                                    idx.numel()))
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
     w = (torch.randn(n, generator=gen, device=dev) * 0.02).to(torch.float16)
@@ -226,7 +229,7 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt):
     w8meta = M.new_meta(1, dev) if level == "O3" else None
     hp = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
     torch.cuda.synchronize()
-    ost = O.TensorState(w[idx].cpu().numpy().view(np.uint16), level)
+    ost = O.TensorState(w[idx].cpu().numpy().view(np.uint16), level, adam=adam)
     stats = {k: Stats() for k in ("m", "v", "w", "w8")}
     M.release_cache()
     for s in (1, 2):
@@ -238,9 +241,10 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt):
         before = M.cache_stats()["bytes"]
         M.profile_enable(True)
         if level == "O2":
-            M.quantize_adamw_o2_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], step=s, **hp)
+            M.quantize_adamw_o2_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], step=s, adam=adam, **hp)
         else:
-            M.quantize_adamw_o3_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], [w8], w8meta, step=s, **hp)
+            M.quantize_adamw_o3_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], [w8], w8meta, step=s, adam=adam,
+                                     **hp)
         torch.cuda.synchronize()
         launches = {k: M.profile_read(k)[0] for k in ("quantize_pass1", "o2_pass2", "o3_pass2", "o3_pass3",
                                                       "finalize")}
