@@ -185,14 +185,17 @@ def test_llama2_7b_fused_adam_2_steps():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("level,gfmt,adam", [("O2", "E4M3", False), ("O3", "E5M2", False), ("O2", "E5M2", True),
-                                             ("O3", "E4M3", True), ("O3", "E5M2", True)])
-def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam):
+@pytest.mark.parametrize("level,gfmt,adam,fused", [
+    ("O2", "E4M3", False, True), ("O3", "E5M2", False, True), ("O2", "E5M2", True, True),
+    ("O3", "E4M3", True, True), ("O3", "E5M2", True, True),
+    ("O3", "E5M2", False, False), ("O2", "E5M2", True, False), ("O3", "E4M3", True, False)])
+def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam, fused):
     """One tensor of exactly 2^30 elements: the smallest list whose step
     passes run the wide launch (512-thread workgroups, 131,072-element
     chunks) and the largest whose 8,192 chunks still fold the meta writes
-    into the last pass (no finalize launch). Two fused quantize-steps (the
-    benchmark's path) checked against the oracle on windows at the start,
+    into the last pass (no finalize launch). Two quantize-steps, fused (the
+    benchmark's path) or as two calls (every wide instantiation of both
+    passes is among the cases), checked against the oracle on windows at the start,
     the middle and the end, with the tensor's largest |gradient| (and, for
     O3, largest |master weight|) planted inside them, so that the oracle run
     on the windows sees the whole tensor's scales (the argument of the
@@ -213,8 +216,8 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam):
     assert all(b <= c for (_, b), (c, _) in zip(wins, wins[1:]))
     assert wins[1][0] <= g_plant < wins[1][1] and wins[0][0] <= w_plant < wins[0][1]
     idx = torch.cat([torch.arange(a, b, device=dev) for a, b in wins])
-    log("%s %s%s: one tensor of 2^30 elements; checking %d of them" % (level, gfmt, " Adam" if adam else "",
-                                                                    idx.numel()))
+    log("%s %s%s%s: one tensor of 2^30 elements; checking %d of them"
+        % (level, gfmt, " Adam" if adam else "", "" if fused else " two calls", idx.numel()))
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
     w = (torch.randn(n, generator=gen, device=dev) * 0.02).to(torch.float16)
@@ -237,20 +240,28 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam):
         x[::2].neg_()
         x[g_plant] = 2.0
         M.amax([x], gmeta)
+        if not fused:
+            M.quantize_fp8([x], fmt, gmeta, [q])
         torch.cuda.synchronize()
         before = M.cache_stats()["bytes"]
         M.profile_enable(True)
-        if level == "O2":
+        if fused and level == "O2":
             M.quantize_adamw_o2_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], step=s, adam=adam, **hp)
-        else:
+        elif fused:
             M.quantize_adamw_o3_step([x], fmt, gmeta, [q], [m], mmeta, [v], [w], [w8], w8meta, step=s, adam=adam,
                                      **hp)
+        elif level == "O2":
+            (M.adam_o2_step if adam else M.adamw_o2_step)([q], fmt, gmeta, [m], mmeta, [v], [w], step=s, **hp)
+        else:
+            (M.adam_o3_step if adam else M.adamw_o3_step)([q], fmt, gmeta, [m], mmeta, [v], [w], [w8], w8meta,
+                                                          step=s, **hp)
         torch.cuda.synchronize()
-        launches = {k: M.profile_read(k)[0] for k in ("quantize_pass1", "o2_pass2", "o3_pass2", "o3_pass3",
-                                                      "finalize")}
+        launches = {k: M.profile_read(k)[0] for k in ("quantize_pass1", "step_pass1", "o2_pass2", "o3_pass2",
+                                                      "o3_pass3", "finalize")}
         M.profile_enable(False)
         assert launches["finalize"] == 0, launches
-        assert launches["quantize_pass1"] == 1 and launches["o3_pass3"] == (1 if level == "O3" else 0), launches
+        assert launches["quantize_pass1" if fused else "step_pass1"] == 1, launches
+        assert launches["o3_pass3"] == (1 if level == "O3" else 0), launches
         if s == 1:
             # the step's tables: 256 B of amax words, 256 B of descriptors and
             # 8,192 chunk references of 8 B (16,384 for 65,536-element chunks)
