@@ -114,7 +114,8 @@ hipError_t timed(msamp_kernel_kind kind, hipStream_t s, F&& launch) {
 // ---------------------------------------------------------- plan cache ---
 
 enum PlanKind : uint64_t {
-  kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3, kPlanQuantizeO2, kPlanQuantizeO3
+  kPlanAmax = 1, kPlanQuantize, kPlanDequantize, kPlanO2, kPlanO3, kPlanQuantizeO2, kPlanQuantizeO3,
+  kPlanKinds  // one past the last kind
 };
 
 // Device tables of one tensor list: amax scratch (two u32 per tensor, kept
@@ -154,7 +155,7 @@ struct PlanCache {
   // the same few lists every step (two gradient buffers, say), so a call
   // first compares its arrays with these in place.
   static constexpr int kRecent = 4;
-  Plan* recent[16][kRecent] = {};
+  Plan* recent[kPlanKinds][kRecent] = {};
 
   void forget(const Plan* p) {
     for (auto& row : recent)
