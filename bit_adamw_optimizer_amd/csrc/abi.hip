@@ -133,7 +133,10 @@ struct Plan {
   TensorDesc* desc = nullptr;
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
-  bool wide = false;  // chunks of kWideChunk for kWideBlock-thread step passes
+  bool wide = false;  // one-tile chunks of kWideChunk for kWideBlock-thread step passes
+  // Workgroups per chunk of the update pass and of the O3 copy (each
+  // chunk's tiles split evenly between them).
+  uint32_t split_update = 1, split_copy = 1;
   uint64_t last_use = 0;
   // Used by a launch captured into a graph: its memory stays until
   // msamp_unpin_captured_tables(), since a replay reads and writes it.
@@ -233,6 +236,61 @@ int64_t list_chunk_elems(int32_t n, const int64_t* numel) { return chunk_tiles_f
 
 bool is_step_plan(uint64_t kind) {
   return kind == kPlanO2 || kind == kPlanO3 || kind == kPlanQuantizeO2 || kind == kPlanQuantizeO3;
+}
+
+// Lists of at most this many chunks write their meta records from the
+// workgroup that completes each tensor (one launch fewer per pass that ends
+// in meta: the launch costs more than the work there); larger lists keep a
+// finalize launch, which avoids one counter atomic per workgroup.
+constexpr int64_t kFoldMaxChunks = 8192;
+
+// Workgroups per chunk of the update pass and of the O3 copy in a list of
+// 16-tile chunks (a large list's step plan has one-tile chunks already):
+// up to kNarrowSplit, or, for a list that folds its meta writes (each
+// workgroup then also counts itself), about kSplitTarget workgroups.
+constexpr uint32_t kNarrowSplit = 16;
+constexpr int64_t kSplitTarget = 16384;
+constexpr uint32_t kMaxFoldSplit = 8;
+
+// Workgroups of a launch over 'ce'-element chunks split 's' ways that get no
+// elements (the parts past each tensor's end).
+int64_t empty_parts(int32_t n, const int64_t* numel, int64_t ce, uint32_t s) {
+  const int64_t span = ce / s;
+  int64_t empty = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    const int64_t chunks = std::max<int64_t>(1, (numel[t] + ce - 1) / ce);
+    empty += chunks * s - (numel[t] + span - 1) / span;
+  }
+  return empty;
+}
+
+// The largest power of two <= want that divides the chunk's tiles, keeps the
+// launch within 2^32 - 1 threads and leaves at most an eighth of the
+// workgroups without elements.
+uint32_t fit_split(uint32_t want, int32_t n, const int64_t* numel, int64_t ce, int64_t nchunks) {
+  uint32_t s = 1;
+  while (s * 2 <= want && (ce / kTile) % (s * 2) == 0 &&
+         nchunks * (int64_t)(s * 2) * kBlock <= (int64_t)UINT32_MAX &&
+         empty_parts(n, numel, ce, s * 2) * 8 <= nchunks * (int64_t)(s * 2))
+    s *= 2;
+  return s;
+}
+
+// Measured on gfx950: smaller workgroups help the passes without a
+// per-workgroup amax reduction (O2 update, O3 copy); the fused pass, pass 1
+// and the O3 update, which reduce an amax in every workgroup, ran slower
+// with 4,096-element workgroups.
+void choose_splits(Plan* p, uint64_t kind, int32_t n, const int64_t* numel, int64_t ce) {
+  if (!is_step_plan(kind) || p->wide || ce != kMaxChunkTiles * kTile) return;
+  const bool fold = p->nchunks <= kFoldMaxChunks;
+  uint32_t want = kNarrowSplit;
+  if (fold) {
+    want = 1;
+    while (want < kMaxFoldSplit && p->nchunks * (int64_t)want * 2 <= kSplitTarget) want *= 2;
+  }
+  const bool o3 = kind == kPlanO3 || kind == kPlanQuantizeO3;
+  if (!o3) p->split_update = fit_split(want, n, numel, ce, p->nchunks);
+  if (o3 && !fold) p->split_copy = fit_split(kNarrowSplit, n, numel, ce, p->nchunks);
 }
 
 // True if 'p' was built for exactly these arrays: the same kind, tensor
@@ -341,7 +399,8 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   }
 
   // Build the chunk map: chunks of list_chunk_elems elements, or of
-  // kWideChunk for the step passes of a large list (wide workgroups).
+  // kWideChunk (one tile of a wide workgroup) for the step passes of a large
+  // list.
   const bool wide = is_step_plan(kind) && list_tiles(n, numel) >= kWideMinTiles;
   const int64_t ce = wide ? kWideChunk : list_chunk_elems(n, numel);
   std::vector<ChunkRef> chunks;
@@ -409,6 +468,7 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
   plan->nchunks = (int64_t)chunks.size();
   plan->wide = wide;
+  choose_splits(plan.get(), kind, n, numel, ce);
 
   e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail_hip(e, "upload of the descriptor tables");
@@ -517,11 +577,6 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
     if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
   } while (0)
 
-// Lists of at most this many chunks write their meta records from the
-// workgroup that completes each tensor (one launch fewer per pass that ends
-// in meta: the launch costs more than the work there); larger lists keep a
-// finalize launch, which avoids one counter atomic per workgroup.
-constexpr int64_t kFoldMaxChunks = 8192;
 
 bool wide_launch(const Plan* p) { return p->wide; }
 
@@ -617,10 +672,11 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev, o3 ? MetaFold{} : fold,
-                                 wide_launch(p)));
+                                 wide_launch(p), p->split_update));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p)));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p),
+                                 p->split_copy));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
@@ -667,10 +723,11 @@ msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t*
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev,
-                                 o3 ? MetaFold{} : fold, wide_launch(p)));
+                                 o3 ? MetaFold{} : fold, wide_launch(p), p->split_update));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p)));
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p),
+                                 p->split_copy));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_step_finalize(n, p->scratch_a, exp_avg_meta, o3 ? p->scratch_b : nullptr,
@@ -789,13 +846,13 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
     MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                  launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                    exp_avg_meta, (const uint32_t*)amax_in, p->scratch_b, k, s, nullptr,
-                                   MetaFold{}, wide_launch(p)));
+                                   MetaFold{}, wide_launch(p), p->split_update));
     if (o3) MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_b, amax_out, s));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_meta_from_amax(n, amax_in, exp_avg_meta, 448.0f, s));
   } else {
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
                  launch_o3_pass3(p->desc, p->chunks, p->nchunks, (const uint32_t*)amax_in, s, MetaFold{},
-                                 wide_launch(p)));
+                                 wide_launch(p), p->split_copy));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_meta_from_amax(n, amax_in, weight_fp8_meta, 448.0f, s));
   }
@@ -1460,7 +1517,8 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
     std::unique_lock<std::mutex> lease;  // held until the launch is enqueued
     const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
     MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
-    MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s, launch_rmw_probe(p->desc, p->chunks, p->nchunks, s, wide_launch(p)));
+    MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s,
+                 launch_rmw_probe(p->desc, p->chunks, p->nchunks, s, wide_launch(p), p->split_update));
     return MSAMP_OK;
   });
 }

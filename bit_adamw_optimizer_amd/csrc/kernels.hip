@@ -6,10 +6,12 @@
 // All kernels are multi-tensor-apply launches: workgroup b takes ChunkRef b
 // (tensor t, chunk j) and covers elements [j*c, min(numel, (j+1)*c)) of
 // tensor t (c: the list's chunk size, in its TensorDesc) in tiles of 16
-// elements per thread: 4,096 elements (4 waves x 1024), or 8,192 (8 waves)
-// for the step passes of a large list. Inside a wave's 1024 elements the lanes are laid
-// out so that every load and store instruction of the wave covers one
-// contiguous span of memory:
+// elements per thread: 4,096 elements (4 waves x 1024), or 8,192 (8 waves,
+// one tile per chunk) for the step passes of a large list. The update pass
+// and the O3 copy may split every chunk evenly over several workgroups
+// (workgroup b then takes part b % split of ChunkRef b / split). Inside a
+// wave's 1024 elements the lanes are laid out so that every load and store
+// instruction of the wave covers one contiguous span of memory:
 //   FP8 / FP16 streams: lane l owns the 8-element groups at l*8 and
 //     512 + l*8 (one 8-byte FP8 access or one 16-byte FP16 access per group)
 //   FP32 streams: lane l owns the 4-element groups at k*256 + l*4, k = 0..3
@@ -79,17 +81,27 @@ __device__ __forceinline__ void block_max2_into(uint32_t a, uint32_t* dst_a, uin
 struct ChunkRange {
   int t;
   int64_t begin, end;
+  bool head;  // the tensor's first workgroup
 };
 
-__device__ __forceinline__ ChunkRange chunk_range(const ChunkRef* chunks, const TensorDesc* desc) {
-  const ChunkRef c = chunks[blockIdx.x];
+// The part of its chunk that this workgroup walks when every chunk is split
+// over 'split' workgroups (blockIdx.x / split is the chunk); the chunk size
+// is a multiple of 'split' tiles, and a part past the tensor's end is empty.
+__device__ __forceinline__ ChunkRange part_range(const ChunkRef* chunks, const TensorDesc* desc, uint32_t split) {
+  const ChunkRef c = chunks[blockIdx.x / split];
+  const uint32_t part = blockIdx.x % split;
   ChunkRange r;
   r.t = c.tensor;
-  const int64_t ce = desc[c.tensor].chunk;
-  r.begin = (int64_t)c.chunk * ce;
+  const int64_t span = desc[c.tensor].chunk / split;
+  r.begin = (int64_t)c.chunk * desc[c.tensor].chunk + (int64_t)part * span;
   const int64_t n = desc[c.tensor].numel;
-  r.end = r.begin + ce < n ? r.begin + ce : n;
+  r.end = r.begin + span < n ? r.begin + span : n;
+  r.head = c.chunk == 0 && part == 0;
   return r;
+}
+
+__device__ __forceinline__ ChunkRange chunk_range(const ChunkRef* chunks, const TensorDesc* desc) {
+  return part_range(chunks, desc, 1u);
 }
 
 // Chunks of a tensor in a plan that folds the meta writes (at least one).
@@ -126,12 +138,12 @@ __device__ __forceinline__ uint32_t take_word(uint32_t* p) {
 // read of the words happened before the workgroup's count (the reads fed
 // the work done since).
 template <bool AMAX_ONLY>
-__device__ __forceinline__ void fold_meta(const MetaFold& f, const TensorDesc* desc, int t) {
+__device__ __forceinline__ void fold_meta(const MetaFold& f, const TensorDesc* desc, int t, uint32_t parts = 1) {
   if (f.done == nullptr) return;
   __syncthreads();
   if (threadIdx.x != 0) return;
   const uint32_t before = __hip_atomic_fetch_add(&f.done[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (before + 1u != chunks_of(desc[t])) return;
+  if (before + 1u != chunks_of(desc[t]) * parts) return;
   const float a = __uint_as_float(take_word(&f.amax_a[t]));
   if (AMAX_ONLY)
     f.meta_a[t].amax = a;
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const TensorDesc* __restric
                                                      msamp_meta* __restrict__ meta, float world) {
   const ChunkRange r = chunk_range(chunks, desc);
   const float s = scale_rule(meta[r.t].amax * world, Fp8Traits<FMT>::kMax);
-  if (chunks[blockIdx.x].chunk == 0 && threadIdx.x == 0) {
+  if (r.head && threadIdx.x == 0) {
     meta[r.t].scale = s;
     meta[r.t].scale_inv = 1.0f / s;
     meta[r.t].reserved = 0.0f;
@@ -412,7 +424,7 @@ __global__ __launch_bounds__(BS) void k_quantize_pass1(const TensorDesc* __restr
   const ChunkRange r = chunk_range(chunks, desc);
   const float s = scale_rule(gmeta[r.t].amax, Fp8Traits<GF>::kMax);
   const float gsi = 1.0f / s;
-  if (chunks[blockIdx.x].chunk == 0 && threadIdx.x == 0) {
+  if (r.head && threadIdx.x == 0) {
     gmeta[r.t].scale = s;
     gmeta[r.t].scale_inv = gsi;
     gmeta[r.t].reserved = 0.0f;
@@ -481,10 +493,10 @@ __global__ __launch_bounds__(BS) void k_step_pass2(const TensorDesc* __restrict_
                                                        uint32_t* __restrict__ amax_w,
                                                        StepConsts kv,
                                                        const StepConsts* __restrict__ kdev,
-                                                       MetaFold fold) {
+                                                       MetaFold fold, uint32_t split) {
   static_assert(!(O3 && DELAYED), "the delayed-scaling ablation is O2 only");
   const StepConsts k = kdev != nullptr ? *kdev : kv;
-  const ChunkRange r = chunk_range(chunks, desc);
+  const ChunkRange r = part_range(chunks, desc, split);
   const float gsi = gmeta[r.t].scale_inv;
   const float msi = mmeta[r.t].scale_inv;
   const float s_m = DELAYED ? scale_rule(mmeta[r.t].amax, kE4M3Max)
@@ -562,15 +574,16 @@ __global__ __launch_bounds__(BS) void k_step_pass2(const TensorDesc* __restrict_
     block_max_into<false, BS>(bits, &amax_w[r.t]);
   }
   if (DELAYED) block_max_into<false, BS>(mmax, &amax_w[r.t]);
-  if (!O3 && !DELAYED) fold_meta<false>(fold, desc, r.t);  // O3: the fold is in pass 3
+  if (!O3 && !DELAYED) fold_meta<false>(fold, desc, r.t, split);  // O3: the fold is in pass 3
 }
 
 // Pass 3 (O3): FP8 E4M3 copy of the stored master with its own scale.
 template <int BS = kBlock>
 __global__ __launch_bounds__(BS) void k_o3_pass3(const TensorDesc* __restrict__ desc,
                                                      const ChunkRef* __restrict__ chunks,
-                                                     const uint32_t* __restrict__ amax_w, MetaFold fold) {
-  const ChunkRange r = chunk_range(chunks, desc);
+                                                     const uint32_t* __restrict__ amax_w, MetaFold fold,
+                                                     uint32_t split) {
+  const ChunkRange r = part_range(chunks, desc, split);
   const float s_w = scale_rule(__uint_as_float(amax_w[r.t]), kE4M3Max);
   const GLOBAL uint16_t* __restrict__ wh = global_ptr<uint16_t>(desc[r.t].p3);
   GLOBAL uint8_t* __restrict__ w8 = global_ptr<uint8_t>(desc[r.t].p4);
@@ -602,7 +615,7 @@ __global__ __launch_bounds__(BS) void k_o3_pass3(const TensorDesc* __restrict__ 
       }
     }
   }
-  fold_meta<false>(fold, desc, r.t);
+  fold_meta<false>(fold, desc, r.t, split);
 }
 
 __global__ __launch_bounds__(kBlock) void k_step_finalize(int32_t n, uint32_t* __restrict__ amax_a,
@@ -799,8 +812,8 @@ __global__ __launch_bounds__(kBlock) void k_delayed_finalize(int32_t n, uint32_t
 // what the memory system gives this traffic on the very same buffers.
 template <int BS = kBlock>
 __global__ __launch_bounds__(BS) void k_rmw_probe(const TensorDesc* __restrict__ desc,
-                                                      const ChunkRef* __restrict__ chunks) {
-  const ChunkRange r = chunk_range(chunks, desc);
+                                                      const ChunkRef* __restrict__ chunks, uint32_t split) {
+  const ChunkRange r = part_range(chunks, desc, split);
   const GLOBAL uint8_t* __restrict__ gq = global_ptr<uint8_t>(desc[r.t].p0);
   GLOBAL uint8_t* __restrict__ mq = global_ptr<uint8_t>(desc[r.t].p1);
   GLOBAL uint16_t* __restrict__ vh = global_ptr<uint16_t>(desc[r.t].p2);
@@ -1056,22 +1069,23 @@ hipError_t launch_step_pass1(int gfmt, bool coupled, const TensorDesc* desc, con
 template <int GF, bool O3, bool COUPLED, int BS>
 static void pass2_launch(unsigned g, hipStream_t stream, const TensorDesc* desc, const ChunkRef* chunks,
                          const msamp_meta* gmeta, const msamp_meta* mmeta, const uint32_t* amax_m,
-                         uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev, const MetaFold& fold) {
+                         uint32_t* amax_w, const StepConsts& k, const StepConsts* kdev, const MetaFold& fold,
+                         uint32_t split) {
   k_step_pass2<GF, O3, COUPLED, false, BS><<<g, BS, 0, stream>>>(desc, chunks, gmeta, mmeta, amax_m, amax_w, k,
-                                                                 kdev, fold);
+                                                                 kdev, fold, split);
 }
 
 template <int GF, int BS>
 static void pass2_dispatch(bool o3, bool coupled, unsigned g, hipStream_t stream,
                            const TensorDesc* desc, const ChunkRef* chunks, const msamp_meta* gmeta,
                            const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
-                           const StepConsts& k, const StepConsts* kdev, const MetaFold& f) {
+                           const StepConsts& k, const StepConsts* kdev, const MetaFold& f, uint32_t sp) {
   if (o3) {
-    if (coupled) pass2_launch<GF, true, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
-    else pass2_launch<GF, true, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    if (coupled) pass2_launch<GF, true, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f, sp);
+    else pass2_launch<GF, true, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f, sp);
   } else {
-    if (coupled) pass2_launch<GF, false, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
-    else pass2_launch<GF, false, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f);
+    if (coupled) pass2_launch<GF, false, true, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f, sp);
+    else pass2_launch<GF, false, false, BS>(g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, f, sp);
   }
 }
 
@@ -1079,19 +1093,24 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
                              const ChunkRef* chunks, int64_t nchunks, const msamp_meta* gmeta,
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                              const StepConsts& k, hipStream_t stream, const StepConsts* kdev,
-                             const MetaFold& fold, bool wide) {
+                             const MetaFold& fold, bool wide, uint32_t split) {
   if (nchunks <= 0) return hipSuccess;
-  const unsigned g = grid_of(nchunks);
+  if (split < 1) return hipErrorInvalidValue;
+  const unsigned g = grid_of(nchunks * split);
   if (gfmt == kE4M3) {
     if (wide)
-      pass2_dispatch<kE4M3, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+      pass2_dispatch<kE4M3, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold,
+                                        split);
     else
-      pass2_dispatch<kE4M3, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+      pass2_dispatch<kE4M3, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold,
+                                    split);
   } else {
     if (wide)
-      pass2_dispatch<kE5M2, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+      pass2_dispatch<kE5M2, kWideBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold,
+                                        split);
     else
-      pass2_dispatch<kE5M2, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold);
+      pass2_dispatch<kE5M2, kBlock>(o3, coupled, g, stream, desc, chunks, gmeta, mmeta, amax_m, amax_w, k, kdev, fold,
+                                    split);
   }
   return hipGetLastError();
 }
@@ -1103,14 +1122,14 @@ hipError_t launch_step_delayed(int gfmt, bool coupled, const TensorDesc* desc, c
   const unsigned g = grid_of(nchunks);
   if (gfmt == kE4M3) {
     if (coupled)
-      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
+      k_step_pass2<kE4M3, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{}, 1u);
     else
-      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
+      k_step_pass2<kE4M3, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{}, 1u);
   } else {
     if (coupled)
-      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
+      k_step_pass2<kE5M2, false, true, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{}, 1u);
     else
-      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{});
+      k_step_pass2<kE5M2, false, false, true><<<g, kBlock, 0, stream>>>(desc, chunks, gmeta, mmeta, nullptr, amax_new, k, nullptr, MetaFold{}, 1u);
   }
   return hipGetLastError();
 }
@@ -1149,12 +1168,15 @@ hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* me
 }
 
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold, bool wide) {
+                           const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold, bool wide,
+                           uint32_t split) {
   if (nchunks <= 0) return hipSuccess;
+  if (split < 1) return hipErrorInvalidValue;
+  const unsigned g = grid_of(nchunks * split);
   if (wide)
-    k_o3_pass3<kWideBlock><<<grid_of(nchunks), kWideBlock, 0, stream>>>(desc, chunks, amax_w, fold);
+    k_o3_pass3<kWideBlock><<<g, kWideBlock, 0, stream>>>(desc, chunks, amax_w, fold, split);
   else
-    k_o3_pass3<kBlock><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks, amax_w, fold);
+    k_o3_pass3<kBlock><<<g, kBlock, 0, stream>>>(desc, chunks, amax_w, fold, split);
   return hipGetLastError();
 }
 
@@ -1210,12 +1232,14 @@ hipError_t launch_qp1_probe(const TensorDesc* desc, const ChunkRef* chunks, int6
 }
 
 hipError_t launch_rmw_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                            hipStream_t stream, bool wide) {
+                            hipStream_t stream, bool wide, uint32_t split) {
   if (nchunks <= 0) return hipSuccess;
+  if (split < 1) return hipErrorInvalidValue;
+  const unsigned g = grid_of(nchunks * split);
   if (wide)
-    k_rmw_probe<kWideBlock><<<grid_of(nchunks), kWideBlock, 0, stream>>>(desc, chunks);
+    k_rmw_probe<kWideBlock><<<g, kWideBlock, 0, stream>>>(desc, chunks, split);
   else
-    k_rmw_probe<kBlock><<<grid_of(nchunks), kBlock, 0, stream>>>(desc, chunks);
+    k_rmw_probe<kBlock><<<g, kBlock, 0, stream>>>(desc, chunks, split);
   return hipGetLastError();
 }
 

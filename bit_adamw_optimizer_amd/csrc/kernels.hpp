@@ -17,12 +17,15 @@ namespace msamp {
 // each tensor carries the chunk size of its list.
 constexpr int kBlock = 256;
 // Large lists (at least kWideMinTiles tiles of kTile) run the step's passes
-// (launchers' 'wide') with kWideBlock-thread workgroups, 8 waves walking
-// 8,192-element tiles, over chunks of kWideChunk elements (16 such tiles):
-// 0.8-1.2% faster on the update and fused passes of the 7B and 13B lists
-// than kBlock threads on kChunk chunks; either change alone gained nothing.
+// (launchers' 'wide') with kWideBlock-thread workgroups, one 8,192-element
+// tile each (chunks of kWideChunk elements). Workgroups that each stream one
+// tile, dispatched in list order, keep the accesses in flight within a
+// narrow window of every stream; on the 7B list this took the update pass
+// from 14.5 to 12.8 ms and the fused pass from 7.4 to 6.8 ms against 16
+// such tiles per workgroup (the amax, a pure read with a reduction per
+// workgroup, ran slower that way and keeps kChunk chunks).
 constexpr int kWideBlock = 512;
-constexpr int64_t kWideChunk = 16 * 16 * (int64_t)kWideBlock;  // 131072 elements
+constexpr int64_t kWideChunk = 16 * (int64_t)kWideBlock;  // 8,192 elements: one tile
 constexpr int64_t kWideMinTiles = (int64_t)16384 * 16;
 constexpr int64_t kTile = (int64_t)kBlock * 16;
 constexpr int64_t kMaxChunkTiles = 16;
@@ -131,7 +134,7 @@ hipError_t launch_step_pass2(int gfmt, bool o3, bool coupled, const TensorDesc* 
                              const msamp_meta* mmeta, const uint32_t* amax_m, uint32_t* amax_w,
                              const StepConsts& k, hipStream_t stream,
                              const StepConsts* kdev = nullptr, const MetaFold& fold = MetaFold{},
-                             bool wide = false);
+                             bool wide = false, uint32_t split = 1);
 // Ablation: the O2 update in one pass with delayed scaling of the first
 // moment (encode with scale(mmeta.amax) of the previous step; reduce the new
 // amax into amax_new).
@@ -144,7 +147,7 @@ hipError_t launch_delayed_finalize(int32_t n, uint32_t* amax_new, msamp_meta* me
                                    hipStream_t stream);
 hipError_t launch_o3_pass3(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
                            const uint32_t* amax_w, hipStream_t stream, const MetaFold& fold = MetaFold{},
-                           bool wide = false);
+                           bool wide = false, uint32_t split = 1);
 // meta_a[t] <- {a, scale(a, 448), 1/scale, 0} with a = amax_a[t], then
 // amax_a[t] <- 0; the same for (amax_b, meta_b) when meta_b is not NULL,
 // with the range fmax_b (448 for an E4M3 copy, 65504 for a scaled FP16 v).
@@ -167,6 +170,6 @@ hipError_t launch_meta_from_amax(int32_t n, const float* amax, msamp_meta* meta,
 // Reads g, m, v, w (roles p0..p3) and writes m, v, w back unchanged, with
 // the same lanes, tiles and launch shape as the O2/O3 update pass.
 hipError_t launch_rmw_probe(const TensorDesc* desc, const ChunkRef* chunks, int64_t nchunks,
-                            hipStream_t stream, bool wide = false);
+                            hipStream_t stream, bool wide = false, uint32_t split = 1);
 
 }  // namespace msamp

@@ -185,39 +185,48 @@ def test_llama2_7b_fused_adam_2_steps():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("level,gfmt,adam,fused", [
-    ("O2", "E4M3", False, True), ("O3", "E5M2", False, True), ("O2", "E5M2", True, True),
-    ("O3", "E4M3", True, True), ("O3", "E5M2", True, True),
-    ("O3", "E5M2", False, False), ("O2", "E5M2", True, False), ("O3", "E4M3", True, False)])
-def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam, fused):
-    """One tensor of exactly 2^30 elements: the smallest list whose step
-    passes run the wide launch (512-thread workgroups, 131,072-element
-    chunks) and the largest whose 8,192 chunks still fold the meta writes
-    into the last pass (no finalize launch). Two quantize-steps, fused (the
+# One tensor of 2^30 elements is the smallest list whose step passes run the
+# wide launch (512-thread workgroups over one-tile chunks of 8,192 elements,
+# 131,072 chunks); one of 10,240 chunks of 65,536 elements (671,088,640
+# elements) is a list of 256-thread workgroups too long to fold its meta
+# writes, whose O2 update pass and O3 copy split every chunk over 16
+# workgroups.
+_WIDE_N, _NARROW_N = 1 << 30, 10240 * 65536
+
+
+@pytest.mark.parametrize("n,level,gfmt,adam,fused", [
+    (_WIDE_N, "O2", "E4M3", False, True), (_WIDE_N, "O3", "E5M2", False, True),
+    (_WIDE_N, "O2", "E5M2", True, True), (_WIDE_N, "O3", "E4M3", True, True), (_WIDE_N, "O3", "E5M2", True, True),
+    (_WIDE_N, "O3", "E5M2", False, False), (_WIDE_N, "O2", "E5M2", True, False),
+    (_WIDE_N, "O3", "E4M3", True, False),
+    (_NARROW_N, "O2", "E4M3", False, True), (_NARROW_N, "O3", "E4M3", False, True),
+    (_NARROW_N, "O2", "E5M2", True, False), (_NARROW_N, "O3", "E5M2", True, False)])
+def test_one_large_tensor_in_each_launch_geometry(n, level, gfmt, adam, fused):
+    """One large tensor (above) through two quantize-steps, fused (the
     benchmark's path) or as two calls (every wide instantiation of both
-    passes is among the cases), checked against the oracle on windows at the start,
-    the middle and the end, with the tensor's largest |gradient| (and, for
-    O3, largest |master weight|) planted inside them, so that the oracle run
-    on the windows sees the whole tensor's scales (the argument of the
-    2^32 + 4099 test above). Gradient magnitudes lie in [0.5, 1], with
-    alternating signs: (1 - beta2) g^2 then stays a normal binary16 number,
-    so no weight takes the large step a zero FP16 second moment gives, and
-    the planted master weight stays the largest. Adam (coupled L2) adds
-    wd * w to each gradient, far below the planted one."""
+    passes is among the cases), checked against the oracle on windows at the
+    start, the middle and the end, with the tensor's largest |gradient|
+    (and, for O3, largest |master weight|) planted inside them, so that the
+    oracle run on the windows sees the whole tensor's scales (the argument
+    of the 2^32 + 4099 test above). Gradient magnitudes lie in [0.5, 1],
+    with alternating signs: (1 - beta2) g^2 then stays a normal binary16
+    number, so no weight takes the large step a zero FP16 second moment
+    gives, and the planted master weight stays the largest. Adam (coupled
+    L2) adds wd * w to each gradient, far below the planted one."""
     import bit_adamw_optimizer_amd as M
     import oracle as O
     from tests.parity import Stats, u32
 
     dev = "cuda"
     fmt = getattr(O, gfmt)
-    n = 1 << 30
-    g_plant, w_plant = (1 << 29) + 77, 1234
-    wins = [(0, 60_000), ((1 << 29) - 60_000, (1 << 29) + 60_000), (n - 60_000, n)]
+    half = n // 2
+    g_plant, w_plant = half + 77, 1234
+    wins = [(0, 60_000), (half - 60_000, half + 60_000), (n - 60_000, n)]
     assert all(b <= c for (_, b), (c, _) in zip(wins, wins[1:]))
     assert wins[1][0] <= g_plant < wins[1][1] and wins[0][0] <= w_plant < wins[0][1]
     idx = torch.cat([torch.arange(a, b, device=dev) for a, b in wins])
-    log("%s %s%s%s: one tensor of 2^30 elements; checking %d of them"
-        % (level, gfmt, " Adam" if adam else "", "" if fused else " two calls", idx.numel()))
+    log("%s %s%s%s: one tensor of %d elements; checking %d of them"
+        % (level, gfmt, " Adam" if adam else "", "" if fused else " two calls", n, idx.numel()))
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
     w = (torch.randn(n, generator=gen, device=dev) * 0.02).to(torch.float16)
@@ -259,13 +268,15 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam, fused):
         launches = {k: M.profile_read(k)[0] for k in ("quantize_pass1", "step_pass1", "o2_pass2", "o3_pass2",
                                                       "o3_pass3", "finalize")}
         M.profile_enable(False)
-        assert launches["finalize"] == 0, launches
+        # more than 8,192 chunks: the meta records come from a finalize launch
+        assert launches["finalize"] == 1, launches
         assert launches["quantize_pass1" if fused else "step_pass1"] == 1, launches
         assert launches["o3_pass3"] == (1 if level == "O3" else 0), launches
         if s == 1:
             # the step's tables: 256 B of amax words, 256 B of descriptors and
-            # 8,192 chunk references of 8 B (16,384 for 65,536-element chunks)
-            assert M.cache_stats()["bytes"] - before == 256 + 256 + 8192 * 8
+            # 8 B per chunk (8,192 elements wide, 65,536 otherwise)
+            chunk = 8192 if n == _WIDE_N else 65536
+            assert M.cache_stats()["bytes"] - before == 256 + 256 + n // chunk * 8
         qg, gm = O.step_tensor(ost, x[idx].cpu().numpy(), fmt, s, **hp)
         assert np.array_equal(u32(gmeta[0, :3].cpu().numpy()), u32(gm[:3])), (gmeta, gm)
         assert np.array_equal(q[idx].cpu().numpy(), qg)
@@ -279,7 +290,7 @@ def test_wide_chunks_with_folded_meta_writes(level, gfmt, adam, fused):
             stats["w8"].add(w8[idx].cpu().numpy(), ost.w8, "fp8", where)
             assert np.array_equal(u32(w8meta[0, :3].cpu().numpy()), u32(ost.w8_meta[:3]))
             assert int(w8[w_plant]) & 0x7F == 0x7E
-        _report("2^30 %s step %d" % (level, s), stats)
+        _report("%d-element %s step %d" % (n, level, s), stats)
     assert_bar(stats)
     del x, q, m, v, w, w8
     torch.cuda.empty_cache()
