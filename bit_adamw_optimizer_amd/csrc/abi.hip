@@ -133,6 +133,11 @@ struct Plan {
   TensorDesc* desc = nullptr;
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
+  // A large list's step plan also holds tables of kWideCoarseChunk-element
+  // chunks, for pass 1 (null otherwise: pass 1 uses desc and chunks).
+  TensorDesc* desc_coarse = nullptr;
+  ChunkRef* chunks_coarse = nullptr;
+  int64_t nchunks_coarse = 0;
   bool wide = false;  // one-tile chunks of kWideChunk for kWideBlock-thread step passes
   // Workgroups per chunk of the update pass and of the O3 copy (each
   // chunk's tiles split evenly between them).
@@ -326,6 +331,27 @@ bool stream_capturing(hipStream_t stream) {
 msamp_status check_list(int32_t n, const int64_t* numel, const void* const* ptrs, const char* role);
 msamp_status check_sizes(int32_t n, const int64_t* numel);
 
+// The chunk map of a list: (tensor, chunk) for every 'ce'-element chunk,
+// and one (empty) chunk for an empty tensor when 'min_one_chunk'.
+msamp_status build_chunk_map(int32_t n, const int64_t* numel, int64_t ce, bool min_one_chunk,
+                             std::vector<ChunkRef>* out) {
+  int64_t total = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    int64_t k = (numel[t] + ce - 1) / ce;
+    if (k == 0 && min_one_chunk) k = 1;
+    if (k > INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "tensor too large for the chunk map");
+    total += k;
+  }
+  if (total > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks for one launch");
+  out->reserve((size_t)total);
+  for (int32_t t = 0; t < n; ++t) {
+    int64_t k = (numel[t] + ce - 1) / ce;
+    if (k == 0 && min_one_chunk) k = 1;
+    for (int64_t j = 0; j < k; ++j) out->push_back({t, (int32_t)j});
+  }
+  return MSAMP_OK;
+}
+
 // Returns the plan of a tensor list, building and uploading it (on 'stream')
 // the first time. 'ptrs' holds 'nroles' pointer arrays (each of length n, or
 // null for a role the operation does not have, whose name is then null too):
@@ -403,21 +429,9 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   // list.
   const bool wide = is_step_plan(kind) && list_tiles(n, numel) >= kWideMinTiles;
   const int64_t ce = wide ? kWideChunk : list_chunk_elems(n, numel);
-  std::vector<ChunkRef> chunks;
-  int64_t total = 0;
-  for (int32_t t = 0; t < n; ++t) {
-    int64_t k = (numel[t] + ce - 1) / ce;
-    if (k == 0 && min_one_chunk) k = 1;
-    if (k > INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "tensor too large for the chunk map");
-    total += k;
-  }
-  if (total > (int64_t)INT32_MAX) return fail(MSAMP_E_INVALID_ARG, "too many chunks for one launch");
-  chunks.reserve((size_t)total);
-  for (int32_t t = 0; t < n; ++t) {
-    int64_t k = (numel[t] + ce - 1) / ce;
-    if (k == 0 && min_one_chunk) k = 1;
-    for (int64_t j = 0; j < k; ++j) chunks.push_back({t, (int32_t)j});
-  }
+  std::vector<ChunkRef> chunks, coarse;
+  MSAMP_TRY(build_chunk_map(n, numel, ce, min_one_chunk, &chunks));
+  if (wide) MSAMP_TRY(build_chunk_map(n, numel, kWideCoarseChunk, min_one_chunk, &coarse));
 
   auto plan = std::make_unique<Plan>();
   plan->device = dev;
@@ -425,7 +439,8 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   const size_t scratch_bytes = align_up(sizeof(uint32_t) * 3 * (size_t)std::max(n, 1), 256);
   const size_t desc_bytes = align_up(sizeof(TensorDesc) * (size_t)std::max(n, 1), 256);
   const size_t chunk_bytes = align_up(sizeof(ChunkRef) * std::max<size_t>(chunks.size(), 1), 256);
-  plan->bytes = scratch_bytes + desc_bytes + chunk_bytes;
+  const size_t coarse_bytes = wide ? desc_bytes + align_up(sizeof(ChunkRef) * std::max<size_t>(coarse.size(), 1), 256) : 0;
+  plan->bytes = scratch_bytes + desc_bytes + chunk_bytes + coarse_bytes;
 
   e = hipMalloc(&plan->dev, plan->bytes);
   if (e != hipSuccess) {
@@ -459,6 +474,16 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   }
   if (!chunks.empty())
     std::memcpy(hb + scratch_bytes + desc_bytes, chunks.data(), chunks.size() * sizeof(ChunkRef));
+  const size_t coarse_at = scratch_bytes + desc_bytes + chunk_bytes;
+  if (wide) {
+    TensorDesc* hc = (TensorDesc*)(hb + coarse_at);
+    for (int32_t t = 0; t < n; ++t) {
+      hc[t] = hd[t];
+      hc[t].chunk = kWideCoarseChunk;
+    }
+    if (!coarse.empty())
+      std::memcpy(hb + coarse_at + desc_bytes, coarse.data(), coarse.size() * sizeof(ChunkRef));
+  }
 
   char* db = (char*)plan->dev;
   plan->scratch_a = (uint32_t*)db;
@@ -467,6 +492,11 @@ msamp_status get_plan(uint64_t kind, int32_t n, const int64_t* numel,
   plan->desc = (TensorDesc*)(db + scratch_bytes);
   plan->chunks = (ChunkRef*)(db + scratch_bytes + desc_bytes);
   plan->nchunks = (int64_t)chunks.size();
+  if (wide) {
+    plan->desc_coarse = (TensorDesc*)(db + coarse_at);
+    plan->chunks_coarse = (ChunkRef*)(db + coarse_at + desc_bytes);
+    plan->nchunks_coarse = (int64_t)coarse.size();
+  }
   plan->wide = wide;
   choose_splits(plan.get(), kind, n, numel, ce);
 
@@ -580,6 +610,19 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
 
 bool wide_launch(const Plan* p) { return p->wide; }
 
+// Tables for pass 1: workgroups of 16 wide tiles on a large list (pass 1
+// reads 2 B/p and reduces an amax in every workgroup; one-tile workgroups
+// made it slower), the plan's own tables otherwise.
+struct Tables {
+  const TensorDesc* desc;
+  const ChunkRef* chunks;
+  int64_t nchunks;
+};
+Tables pass1_tables(const Plan* p) {
+  if (p->desc_coarse != nullptr) return {p->desc_coarse, p->chunks_coarse, p->nchunks_coarse};
+  return {p->desc, p->chunks, p->nchunks};
+}
+
 // The meta writes of a step folded into its last pass (pass 2 for O2,
 // pass 3 for O3), or none for a large list.
 MetaFold step_fold(const Plan* p, bool o3, msamp_meta* exp_avg_meta, msamp_meta* weight_fp8_meta) {
@@ -665,8 +708,9 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   MSAMP_TRY(step_plan(o3, n, numel, grad, exp_avg, exp_avg_sq, weight, weight_fp8, s, &p, &lease));
   const StepConsts k = kdev == nullptr ? make_consts(hp, step, coupled) : StepConsts{};
 
+  const Tables t1 = pass1_tables(p);
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
-               launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
+               launch_step_pass1(grad_fmt, coupled, t1.desc, t1.chunks, t1.nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, k, s, kdev, wide_launch(p)));
   const MetaFold fold = step_fold(p, o3, exp_avg_meta, weight_fp8_meta);
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
@@ -757,8 +801,9 @@ msamp_status step_scaled_v_impl(int32_t n, const int64_t* numel, const uint8_t* 
   const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
   MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
   const StepConsts k = make_consts(hp, step, false);
+  const Tables t1 = pass1_tables(p);
   MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
-               launch_scaled_v_pass1(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
+               launch_scaled_v_pass1(grad_fmt, t1.desc, t1.chunks, t1.nchunks, grad_meta,
                                      exp_avg_meta, exp_avg_sq_meta, p->scratch_a, p->scratch_b, k, s));
   MSAMP_LAUNCH(MSAMP_KERNEL_O2_PASS2, s,
                launch_scaled_v_pass2(grad_fmt, p->desc, p->chunks, p->nchunks, grad_meta,
@@ -835,8 +880,9 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
   MSAMP_TRY(step_plan(o3, n, numel, grad, exp_avg, exp_avg_sq, weight, weight_fp8, s, &p, &lease));
   if (phase == 1) {
     const StepConsts k = make_consts(hp, step, coupled);
+    const Tables t1 = pass1_tables(p);
     MSAMP_LAUNCH(MSAMP_KERNEL_STEP_PASS1, s,
-                 launch_step_pass1(grad_fmt, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
+                 launch_step_pass1(grad_fmt, coupled, t1.desc, t1.chunks, t1.nchunks, grad_meta,
                                    exp_avg_meta, p->scratch_a, k, s, nullptr, wide_launch(p)));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_a, amax_out, s));
   } else if (phase == 2) {

@@ -274,9 +274,14 @@ def test_one_large_tensor_in_each_launch_geometry(n, level, gfmt, adam, fused):
         assert launches["o3_pass3"] == (1 if level == "O3" else 0), launches
         if s == 1:
             # the step's tables: 256 B of amax words, 256 B of descriptors and
-            # 8 B per chunk (8,192 elements wide, 65,536 otherwise)
-            chunk = 8192 if n == _WIDE_N else 65536
-            assert M.cache_stats()["bytes"] - before == 256 + 256 + n // chunk * 8
+            # 8 B per chunk (8,192 elements wide, 65,536 otherwise); a wide
+            # list adds descriptors and a map of 131,072-element chunks for
+            # pass 1
+            if n == _WIDE_N:
+                expect = 256 + 256 + n // 8192 * 8 + 256 + n // 131072 * 8
+            else:
+                expect = 256 + 256 + n // 65536 * 8
+            assert M.cache_stats()["bytes"] - before == expect
         qg, gm = O.step_tensor(ost, x[idx].cpu().numpy(), fmt, s, **hp)
         assert np.array_equal(u32(gmeta[0, :3].cpu().numpy()), u32(gm[:3])), (gmeta, gm)
         assert np.array_equal(q[idx].cpu().numpy(), qg)
