@@ -1544,7 +1544,8 @@ msamp_status msamp_stream_probe(msamp_stream_kind kind, const void* src, void* d
       if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
         return fail(MSAMP_E_INVALID_ARG, "src and dst overlap");
     }
-    if (bytes / 16 / (16 * 1024) >= (int64_t)UINT32_MAX) return fail(MSAMP_E_INVALID_ARG, "bytes too large");
+    // one 256-thread workgroup per 16 KB: the launch must stay within 2^32 - 1 threads
+    if ((bytes / 16 + 1023) / 1024 * 256 > (int64_t)UINT32_MAX) return fail(MSAMP_E_INVALID_ARG, "bytes too large");
     hipStream_t s = (hipStream_t)stream;
     MSAMP_LAUNCH(copy ? MSAMP_KERNEL_COPY_PROBE : MSAMP_KERNEL_READ_PROBE, s,
                  launch_stream_probe(copy, src, dst, bytes, s));

@@ -889,10 +889,11 @@ __global__ __launch_bounds__(BS) void k_qp1_probe(const TensorDesc* __restrict__
 
 // Plain streams over one buffer in 16-byte units (measurement aid): the
 // lanes of the amax kernel's FP32 layout (each wave instruction covers 1 KB
-// of consecutive memory, 16 KB per tile, 256 KB per workgroup), non-temporal
+// of consecutive memory), one 16 KB tile per workgroup (a copy ran 7% faster
+// that way than with 16 tiles per workgroup, a read 1-2%), non-temporal
 // loads and stores. READ only loads (the empty asm keeps the loaded values
 // live, so the loads are issued and waited for); COPY stores what it loads.
-constexpr int64_t kProbeTileUnits = 1024, kProbeChunkUnits = 16 * kProbeTileUnits;
+constexpr int64_t kProbeTileUnits = 1024, kProbeChunkUnits = kProbeTileUnits;
 
 template <bool COPY>
 __global__ __launch_bounds__(kBlock) void k_stream_probe(const u32x4* __restrict__ src_p,

@@ -549,8 +549,8 @@ msamp_status msamp_quantize_pass1_probe(int32_t n, const int64_t* numel, const f
 
 /*
  * msamp_stream_probe -- MEASUREMENT AID, not part of the method: a plain
- * stream at the launch shape of the library's kernels (16-byte accesses,
- * each wave instruction on 1 KB of consecutive memory, 256 KB per
+ * stream at the access shape of the library's kernels (16-byte accesses,
+ * each wave instruction on 1 KB of consecutive memory, one 16 KB tile per
  * workgroup, non-temporal hints), giving the rates the memory system offers
  * a pure read and a copy, beside msamp_rmw_probe's read-modify-write:
  *   MSAMP_STREAM_READ  reads 'bytes' from src; dst is not used (may be NULL)

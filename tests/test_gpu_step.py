@@ -304,6 +304,22 @@ def test_rmw_probe_leaves_every_stream_unchanged():
     assert all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(after, before))
 
 
+def test_stream_probe_copies_exactly_and_leaves_the_source():
+    """msamp_stream_probe (measurement aid): a copy reproduces the source byte
+    for byte, over whole 16 KB workgroup tiles and a ragged last one, writes
+    nothing past the copied bytes, and neither kind changes the source."""
+    for nbytes in (16, 16 * 1024, 16 * 1024 * 37 + 48):
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+        keep = src.clone()
+        dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+        M.stream_probe(src)
+        M.stream_probe(src, dst[:nbytes])
+        torch.cuda.synchronize()
+        assert torch.equal(src, keep)
+        assert torch.equal(dst[:nbytes], src)
+        assert int(dst[nbytes:].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("level,adam,wl,fused", [("O2", False, "tiny_llama", False),
                                                  ("O3", True, "tiny_llama_o3", False),
                                                  ("O2", False, "tiny_stress", False),
