@@ -232,6 +232,10 @@ msamp_status msamp_adamw_o2_step(int32_t n, const int64_t* numel, const uint8_t*
  * C = 4096 * clamp(floor(T / 1024), 1, 16) with T = sum_t ceil(numel[t] /
  * 4096): 65,536, or fewer for a list under 16,384 tiles (about 67M
  * elements), so that small lists still spread over every compute unit.
+ * Large lists keep these chunks here, while msamp_adamw_o2_step runs their
+ * passes over one-tile chunks (tables 8x larger than this array allows for
+ * the 7B list) and splits the update pass of mid-size lists; the results
+ * are the same, the update pass of such lists is slower here.
  * Limit: round256(8 n) + round256(64 n) + 8 * sum_t ceil(numel[t] / C)
  * <= MSAMP_NOALLOC_SCRATCH_BYTES (the Llama-2-13B list, 363 tensors and
  * 13.0e9 parameters, needs 1.6 MB); a larger list returns
