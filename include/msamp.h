@@ -528,8 +528,10 @@ msamp_status msamp_codec_probe(msamp_probe_op op, const void* in, void* out, int
  * and w of an O2 step's tensor lists (or g, m, v and the master of an O3
  * list) and writes m, v and w back UNCHANGED, with the lanes, tiles and
  * launch shape of the update pass but none of its arithmetic: 6 bytes read
- * and 5 written per element. Its rate on the caller's own buffers is the
- * ceiling the memory system gives the update pass's traffic there. Arguments
+ * and 5 written per element. Its rate on the caller's own buffers is what
+ * the memory system gives that traffic alone there: a reference for the
+ * update pass, not a bound (the pass, whose arithmetic spaces out its
+ * accesses, can run faster). Arguments
  * as msamp_adamw_o2_step; the same work must not run concurrently on these
  * tensors.
  */
@@ -543,7 +545,8 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
  * msamp_quantize_adamw_o2_step without its arithmetic (same lanes, tiles and
  * launch): reads grad_f32 and exp_avg, and writes UNSPECIFIED values to the
  * gradient codes 'grad' (6 bytes per element). Its rate on the caller's own
- * buffers is the ceiling the memory system gives that pass there. Arguments
+ * buffers is what the memory system gives that traffic alone there (a
+ * reference, not a bound). Arguments
  * and errors as msamp_quantize_adamw_o2_step (the lists must be the ones a
  * quantizing step uses, with exp_avg_sq and weight); no meta is touched.
  */
