@@ -140,8 +140,10 @@ struct Plan {
   int64_t nchunks_coarse = 0;
   bool wide = false;  // one-tile chunks of kWideChunk for kWideBlock-thread step passes
   // Workgroups per chunk of the update pass and of the O3 copy (each
-  // chunk's tiles split evenly between them).
+  // chunk's tiles split evenly between them), and whether those split
+  // launches run kWideBlock-thread workgroups.
   uint32_t split_update = 1, split_copy = 1;
+  bool wide_update = false, wide_copy = false;
   uint64_t last_use = 0;
   // Used by a launch captured into a graph: its memory stays until
   // msamp_unpin_captured_tables(), since a replay reads and writes it.
@@ -250,12 +252,12 @@ bool is_step_plan(uint64_t kind) {
 constexpr int64_t kFoldMaxChunks = 8192;
 
 // Workgroups per chunk of the update pass and of the O3 copy in a list of
-// 16-tile chunks (a large list's step plan has one-tile chunks already):
-// up to kNarrowSplit, or, for a list that folds its meta writes (each
-// workgroup then also counts itself), about kSplitTarget workgroups.
-constexpr uint32_t kNarrowSplit = 16;
+// 16-tile chunks (a large list's step plan has one-tile chunks already), of
+// kSplitBlock threads: one tile each, or, for a list that folds its meta
+// writes (each workgroup then also counts itself), about kSplitTarget
+// workgroups in all.
+constexpr int kSplitBlock = kWideBlock;
 constexpr int64_t kSplitTarget = 16384;
-constexpr uint32_t kMaxFoldSplit = 8;
 
 // Workgroups of a launch over 'ce'-element chunks split 's' ways that get no
 // elements (the parts past each tensor's end).
@@ -269,13 +271,13 @@ int64_t empty_parts(int32_t n, const int64_t* numel, int64_t ce, uint32_t s) {
   return empty;
 }
 
-// The largest power of two <= want that divides the chunk's tiles, keeps the
-// launch within 2^32 - 1 threads and leaves at most an eighth of the
-// workgroups without elements.
-uint32_t fit_split(uint32_t want, int32_t n, const int64_t* numel, int64_t ce, int64_t nchunks) {
+// The largest power of two <= want that divides the chunk's tiles (of
+// 'block' threads), keeps the launch within 2^32 - 1 threads and leaves at
+// most an eighth of the workgroups without elements.
+uint32_t fit_split(uint32_t want, int32_t n, const int64_t* numel, int64_t ce, int64_t nchunks, int block) {
+  const int64_t tiles = ce / ((int64_t)block * 16);
   uint32_t s = 1;
-  while (s * 2 <= want && (ce / kTile) % (s * 2) == 0 &&
-         nchunks * (int64_t)(s * 2) * kBlock <= (int64_t)UINT32_MAX &&
+  while (s * 2 <= want && tiles % (s * 2) == 0 && nchunks * (int64_t)(s * 2) * block <= (int64_t)UINT32_MAX &&
          empty_parts(n, numel, ce, s * 2) * 8 <= nchunks * (int64_t)(s * 2))
     s *= 2;
   return s;
@@ -284,18 +286,21 @@ uint32_t fit_split(uint32_t want, int32_t n, const int64_t* numel, int64_t ce, i
 // Measured on gfx950: smaller workgroups help the passes without a
 // per-workgroup amax reduction (O2 update, O3 copy); the fused pass, pass 1
 // and the O3 update, which reduce an amax in every workgroup, ran slower
-// with 4,096-element workgroups.
+// with one-tile workgroups on lists of this size.
 void choose_splits(Plan* p, uint64_t kind, int32_t n, const int64_t* numel, int64_t ce) {
   if (!is_step_plan(kind) || p->wide || ce != kMaxChunkTiles * kTile) return;
+  const uint32_t tiles = (uint32_t)(ce / ((int64_t)kSplitBlock * 16));
   const bool fold = p->nchunks <= kFoldMaxChunks;
-  uint32_t want = kNarrowSplit;
+  uint32_t want = tiles;
   if (fold) {
     want = 1;
-    while (want < kMaxFoldSplit && p->nchunks * (int64_t)want * 2 <= kSplitTarget) want *= 2;
+    while (want < tiles && p->nchunks * (int64_t)want * 2 <= kSplitTarget) want *= 2;
   }
   const bool o3 = kind == kPlanO3 || kind == kPlanQuantizeO3;
-  if (!o3) p->split_update = fit_split(want, n, numel, ce, p->nchunks);
-  if (o3 && !fold) p->split_copy = fit_split(kNarrowSplit, n, numel, ce, p->nchunks);
+  if (!o3) p->split_update = fit_split(want, n, numel, ce, p->nchunks, kSplitBlock);
+  if (o3 && !fold) p->split_copy = fit_split(tiles, n, numel, ce, p->nchunks, kSplitBlock);
+  p->wide_update = kSplitBlock == kWideBlock && p->split_update > 1;
+  p->wide_copy = kSplitBlock == kWideBlock && p->split_copy > 1;
 }
 
 // True if 'p' was built for exactly these arrays: the same kind, tensor
@@ -612,6 +617,8 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
 
 
 bool wide_launch(const Plan* p) { return p->wide; }
+bool wide_update(const Plan* p) { return p->wide || p->wide_update; }
+bool wide_copy(const Plan* p) { return p->wide || p->wide_copy; }
 
 // Tables for pass 1: workgroups of 16 wide tiles on a large list (pass 1
 // reads 2 B/p and reduces an amax in every workgroup; one-tile workgroups
@@ -719,10 +726,10 @@ msamp_status step_impl(bool o3, bool coupled, int32_t n, const int64_t* numel, c
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev, o3 ? MetaFold{} : fold,
-                                 wide_launch(p), p->split_update));
+                                 wide_update(p), p->split_update));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p),
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_copy(p),
                                  p->split_copy));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
@@ -770,10 +777,10 @@ msamp_status quantize_step_impl(bool o3, bool coupled, int32_t n, const int64_t*
   MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                  exp_avg_meta, p->scratch_a, p->scratch_b, k, s, kdev,
-                                 o3 ? MetaFold{} : fold, wide_launch(p), p->split_update));
+                                 o3 ? MetaFold{} : fold, wide_update(p), p->split_update));
   if (o3)
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
-                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_launch(p),
+                 launch_o3_pass3(p->desc, p->chunks, p->nchunks, p->scratch_b, s, fold, wide_copy(p),
                                  p->split_copy));
   if (fold.done == nullptr)
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
@@ -895,13 +902,13 @@ msamp_status phase_impl(int phase, bool o3, bool coupled, int32_t n, const int64
     MSAMP_LAUNCH(o3 ? MSAMP_KERNEL_O3_PASS2 : MSAMP_KERNEL_O2_PASS2, s,
                  launch_step_pass2(grad_fmt, o3, coupled, p->desc, p->chunks, p->nchunks, grad_meta,
                                    exp_avg_meta, (const uint32_t*)amax_in, p->scratch_b, k, s, nullptr,
-                                   MetaFold{}, wide_launch(p), p->split_update));
+                                   MetaFold{}, wide_update(p), p->split_update));
     if (o3) MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_export_amax(n, p->scratch_b, amax_out, s));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s, launch_meta_from_amax(n, amax_in, exp_avg_meta, 448.0f, s));
   } else {
     MSAMP_LAUNCH(MSAMP_KERNEL_O3_PASS3, s,
                  launch_o3_pass3(p->desc, p->chunks, p->nchunks, (const uint32_t*)amax_in, s, MetaFold{},
-                                 wide_launch(p), p->split_copy));
+                                 wide_copy(p), p->split_copy));
     MSAMP_LAUNCH(MSAMP_KERNEL_FINALIZE, s,
                  launch_meta_from_amax(n, amax_in, weight_fp8_meta, 448.0f, s));
   }
@@ -1568,7 +1575,7 @@ msamp_status msamp_rmw_probe(int32_t n, const int64_t* numel, const uint8_t* con
     const char* names[4] = {"grad", "exp_avg", "exp_avg_sq", "weight"};
     MSAMP_TRY(get_plan(kPlanO2, n, numel, roles, names, 4, true, s, &p, &lease));
     MSAMP_LAUNCH(MSAMP_KERNEL_RMW_PROBE, s,
-                 launch_rmw_probe(p->desc, p->chunks, p->nchunks, s, wide_launch(p), p->split_update));
+                 launch_rmw_probe(p->desc, p->chunks, p->nchunks, s, wide_update(p), p->split_update));
     return MSAMP_OK;
   });
 }
