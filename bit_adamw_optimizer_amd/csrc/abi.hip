@@ -134,7 +134,8 @@ struct Plan {
   ChunkRef* chunks = nullptr;
   int64_t nchunks = 0;
   // A large list's step plan also holds tables of kWideCoarseChunk-element
-  // chunks, for pass 1 (null otherwise: pass 1 uses desc and chunks).
+  // chunks, for pass 1 and the scaled-v ablation's pass 1 (null otherwise:
+  // those use desc and chunks).
   TensorDesc* desc_coarse = nullptr;
   ChunkRef* chunks_coarse = nullptr;
   int64_t nchunks_coarse = 0;
@@ -614,7 +615,6 @@ StepConsts make_consts(const msamp_adamw_hparams* hp, int64_t step, bool coupled
     hipError_t e__ = timed((kind), (stream), [&]() { return (call); });   \
     if (e__ != hipSuccess) return fail_hip(e__, msamp_kernel_name(kind));  \
   } while (0)
-
 
 bool wide_launch(const Plan* p) { return p->wide; }
 bool wide_update(const Plan* p) { return p->wide || p->wide_update; }
