@@ -201,3 +201,45 @@ def test_concurrent_threads_with_plan_eviction():
     for th in threads:
         th.join()
     assert not errors, errors[:3]
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_large_list_casts_one_tile_per_workgroup(fmt):
+    """A list of at least 262,144 tiles runs the quantize and dequantize casts
+    one 4,096-element tile per workgroup: a tensor of 2^30 + 4,099 elements
+    (ragged end) and a small one, checked bit for bit against the oracle on
+    windows at the start, the middle and the end, with the large tensor's
+    largest |x| planted inside them (so the oracle sees its amax)."""
+    n = (1 << 30) + 4099
+    plant = (1 << 29) + 11
+    wins = [(0, 50_000), ((1 << 29) - 50_000, (1 << 29) + 50_000), (n - 50_000, n)]
+    idx = torch.cat([torch.arange(a, b, device=DEV) for a, b in wins])
+    log("large-list casts fmt=%d: %d + 1000 elements, checking %d" % (fmt, n, idx.numel()))
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77 + fmt)
+    x = torch.empty(n, dtype=torch.float32, device=DEV)
+    x.uniform_(-1e-2, 1e-2, generator=gen)
+    x[plant] = -0.75
+    small = torch.randn(1000, generator=gen, device=DEV) * 1e-3
+    meta = M.new_meta(2, DEV)
+    q = [torch.empty(n, dtype=torch.uint8, device=DEV), torch.empty(1000, dtype=torch.uint8, device=DEV)]
+    out = [torch.empty(n, dtype=torch.float32, device=DEV), torch.empty(1000, dtype=torch.float32, device=DEV)]
+    M.amax([x, small], meta)
+    M.quantize_fp8([x, small], fmt, meta, q)
+    M.dequantize_fp8(q, fmt, meta, out)
+    torch.cuda.synchronize()
+    mg = meta.cpu().numpy()
+    xw = x[idx].cpu().numpy()
+    assert u32(mg[0, 0]) == u32(O.amax(xw)) == u32(np.float32(0.75))
+    qr, mr = O.quantize_fp8(xw, fmt, amax_value=mg[0, 0])
+    assert np.array_equal(u32(mg[0, :3]), u32(mr[:3])), (mg[0], mr)
+    assert np.array_equal(q[0][idx].cpu().numpy(), qr)
+    dr = O.dequantize_fp8(qr, fmt, mr[2])
+    assert np.array_equal(out[0][idx].cpu().numpy().view(np.uint32), dr.view(np.uint32))
+    xs = small.cpu().numpy()
+    qs, ms = O.quantize_fp8(xs, fmt)
+    assert np.array_equal(u32(mg[1, :3]), u32(ms[:3]))
+    assert np.array_equal(q[1].cpu().numpy(), qs)
+    assert np.array_equal(out[1].cpu().numpy().view(np.uint32), O.dequantize_fp8(qs, fmt, ms[2]).view(np.uint32))
+    del x, q, out
+    torch.cuda.empty_cache()
